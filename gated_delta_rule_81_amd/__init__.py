@@ -1,0 +1,11 @@
+"""Kimi Delta Attention (KDA) forward on AMD Instinct MI355X (gfx950).
+
+Python front end of ``libkda.so``; the C ABI is declared in include/kda.h.
+
+    out, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+    out = decode_step(q, k, v, log_alpha, beta, state)   # state updated in place
+"""
+from ._lib import KdaError, lib
+from .ops import chunk_fwd, decode_step
+
+__all__ = ["chunk_fwd", "decode_step", "KdaError", "lib"]

@@ -1,0 +1,154 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument validation on
+// the host, then one kernel launch on the caller's stream.
+//
+// Validation order: NULL pointers, sizes, supported configurations,
+// alignment, aliasing (all pure host checks, no HIP call), then the device
+// architecture (cached per device), then the launch.
+#include "kda.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+bool aligned16(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void *p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+struct Range {
+    const void *p;
+    uint64_t bytes;
+};
+
+bool overlap(const Range &a, const Range &b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KDA_ERR_DEVICE;
+    if (dev >= kMaxDevices) return KDA_ERR_DEVICE;
+    int st = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KDA_ERR_DEVICE;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_device_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char *kda_status_string(int status) {
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is negative or the sizes disagree";
+    case KDA_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case KDA_ERR_ALIGN: return "a pointer is not aligned as the ABI requires";
+    case KDA_ERR_ALIAS: return "an output overlaps an input";
+    case KDA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  void *out, float *final_state, int32_t batch, int32_t seq_len,
+                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
+                  int32_t dtype, hipStream_t stream) {
+    // sizes
+    if (batch < 0 || seq_len < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0)
+        return KDA_ERR_SHAPE;
+    if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && (batch != 1 || num_seqs < 0)) return KDA_ERR_SHAPE;
+    const int64_t tokens = (int64_t)batch * seq_len;
+    if (tokens > INT32_MAX) return KDA_ERR_SHAPE;
+    const int64_t nseq = packed ? num_seqs : batch;
+    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
+    const uint64_t th = (uint64_t)tokens * num_heads;
+    // pointers required whenever the array they describe is not empty
+    const bool have_tokens = th > 0;
+    if (have_tokens && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERR_NULL;
+    // supported configurations
+    if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
+    const int d = head_dim_k;
+    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if (dtype == kda::kDtypeF32 && d != 64) return KDA_ERR_UNSUPPORTED;
+    // alignment
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        !aligned4(beta) || !aligned16(initial_state) || !aligned16(out) ||
+        !aligned16(final_state) || !aligned4(cu_seqlens))
+        return KDA_ERR_ALIGN;
+    // aliasing
+    const uint64_t state_bytes = (uint64_t)nseq * num_heads * d * d * 4;
+    const Range rq{q, th * d * esz}, rk{k, th * d * esz}, rv{v, th * d * esz},
+        rg{log_alpha, th * d * 4}, rb{beta, th * 4}, rs0{initial_state, state_bytes},
+        rcu{cu_seqlens, packed ? (uint64_t)(nseq + 1) * 4 : 0}, ro{out, th * d * esz},
+        rs1{final_state, state_bytes};
+    const Range inputs[] = {rq, rk, rv, rg, rb, rs0, rcu};
+    for (const Range &r : inputs)
+        if (overlap(ro, r)) return KDA_ERR_ALIAS;
+    if (overlap(ro, rs1)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i) {
+        if (i == 5 && final_state && (const void *)final_state == (const void *)initial_state)
+            continue;  // in-place state update is allowed
+        if (overlap(rs1, inputs[i])) return KDA_ERR_ALIAS;
+    }
+    if (nseq == 0 || num_heads == 0) return KDA_OK;
+    const int st = check_device();
+    if (st != KDA_OK) return st;
+    const int rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+                                         final_state, (int32_t)nseq, seq_len, (int32_t)tokens,
+                                         num_heads, d, dtype, stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                    const float *beta, float *state, void *out, int32_t batch, int32_t num_heads,
+                    int32_t head_dim_k, int32_t head_dim_v, int32_t dtype, hipStream_t stream) {
+    if (batch < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0) return KDA_ERR_SHAPE;
+    if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
+    const uint64_t units = (uint64_t)batch * num_heads;
+    if (units > 0 && (!q || !k || !v || !log_alpha || !beta || !state || !out))
+        return KDA_ERR_NULL;
+    if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
+    const int d = head_dim_k;
+    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        !aligned4(beta) || !aligned16(state) || !aligned16(out))
+        return KDA_ERR_ALIGN;
+    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
+    const Range ro{out, units * d * esz};
+    const Range others[] = {{q, units * d * esz}, {k, units * d * esz}, {v, units * d * esz},
+                            {log_alpha, units * d * 4}, {beta, units * 4},
+                            {state, units * d * d * 4}};
+    for (const Range &r : others)
+        if (overlap(ro, r)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(others[5], others[i])) return KDA_ERR_ALIAS;
+    if (units == 0) return KDA_OK;
+    const int st = check_device();
+    if (st != KDA_OK) return st;
+    const int rc = kda::launch_decode_step(q, k, v, log_alpha, beta, state, out, (int64_t)units,
+                                           d, dtype, stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// kda_internal.h -- host-side launch functions shared by the library's
+// translation units (not part of the public ABI; see include/kda.h).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBf16 = 1;
+
+// Queue one decode step for `units` = B * H (session, head) pairs whose
+// arguments were already validated.  Returns 0, or -1 if the launch failed.
+int launch_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                       const float *beta, float *state, void *out, int64_t units, int head_dim,
+                       int dtype, hipStream_t stream);
+
+// Queue the chunked prefill.  Dense when cu_seqlens == NULL (num_seqs = batch
+// sequences of seq_len tokens each); packed otherwise (batch == 1).  Arguments
+// are already validated.  Returns 0, or -1 if the launch failed.
+int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                     void *out, float *final_state, int32_t num_seqs, int32_t seq_len,
+                     int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
+                     hipStream_t stream);
+
+}  // namespace kda

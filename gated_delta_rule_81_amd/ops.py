@@ -1,0 +1,118 @@
+"""PyTorch front end of the KDA library: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/kda.h); this module checks tensor metadata, allocates outputs with
+torch (device memory) and passes raw pointers plus torch's current stream.
+
+Pages cited (by title):
+  [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (§四: the update).
+  [K3-memory]     "Kimi K3 Changed the Memory Math for Agentic AI Forever" (§3:
+                  the [batch, heads, value_dim, key_dim] state layout).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import KDA_DTYPE_BF16, KDA_DTYPE_F32, check, lib
+
+_DTYPES = {torch.float32: KDA_DTYPE_F32, torch.bfloat16: KDA_DTYPE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _expect(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill (``kda_chunk_fwd``).
+
+    q, k, log_alpha: [B, T, H, d_k]; v: [B, T, H, d_v]; beta: [B, T, H];
+    initial_state: [N, H, d_v, d_k] fp32 or None (zeros); cu_seqlens: int32
+    [N + 1] on the device for packed sequences (then B must be 1), else None
+    and N = B.  q, k, v share one dtype (float32 or bfloat16); gates and
+    states are float32.  Returns (out [B, T, H, d_v], final_state or None).
+    ``final_state`` may be passed in (and may be ``initial_state`` itself).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _expect(q, "q", q.dtype, (B, T, H, dk), dev)
+    _expect(k, "k", q.dtype, (B, T, H, dk), dev)
+    _expect(v, "v", q.dtype, (B, T, H, dv), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    _expect(beta, "beta", torch.float32, (B, T, H), dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be 1-D")
+        _expect(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    _expect(initial_state, "initial_state", torch.float32, (N, H, dv, dk), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _expect(out, "out", q.dtype, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    _expect(final_state, "final_state", torch.float32, (N, H, dv, dk), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), _ptr(out), _ptr(final_state), B, T, H, dk, dv,
+        N if cu_seqlens is not None else 0, _DTYPES[q.dtype], stream)
+    check(rc, "kda_chunk_fwd")
+    return out, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None
+                ) -> torch.Tensor:
+    """One decode token per session (``kda_decode_step``), state updated in place.
+
+    q, k, log_alpha: [B, H, d_k]; v: [B, H, d_v]; beta: [B, H];
+    state: [B, H, d_v, d_k] fp32.  Returns out [B, H, d_v] (dtype of q).
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d_k]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _expect(k, "k", q.dtype, (B, H, dk), dev)
+    _expect(v, "v", q.dtype, (B, H, dv), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (B, H, dk), dev)
+    _expect(beta, "beta", torch.float32, (B, H), dev)
+    _expect(state, "state", torch.float32, (B, H, dv, dk), dev)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _expect(out, "out", q.dtype, (B, H, dv), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                               _ptr(state), _ptr(out), B, H, dk, dv, _DTYPES[q.dtype], stream)
+    check(rc, "kda_decode_step")
+    return out

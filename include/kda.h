@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) forward pass on
+ * AMD Instinct MI355X (gfx950), hand-written HIP.
+ *
+ * Pages cited (by title):
+ *   [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (KDA equations).
+ *   [K3-memory]     "Kimi K3 Changed the Memory Math for Agentic AI Forever"
+ *                   (hubwiz.com translation, "Kimi K3 混合线性注意力").
+ *   [Kimi-Linear]   "Kimi Linear 最多砍掉 75% KV Cache：全注意力真要退场了吗？"
+ *                   (ai.concitech.org).
+ *
+ * What the library computes.  For every sequence and head it keeps one state
+ * S in R^{d_k x d_v} ([K3-explainer] §二.1) and applies, token by token,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,
+ *
+ * the KDA update of [K3-explainer] §四 (per-channel decay alpha_t in
+ * [0,1]^{d_k}, scalar write strength beta_t) with the read of §二.1.  There is
+ * no 1/sqrt(d_k) scale and no normalisation of q or k inside the library.
+ *
+ * Conventions shared by every entry point:
+ *   - Gates are passed as natural logs: alpha_t[c] = exp(log_alpha[t,h,c]).
+ *   - States are fp32 and stored transposed, M = S^T, shape [.., H, d_v, d_k]
+ *     (row = value channel, contiguous along the key channel): the
+ *     [batch, heads, value_dim, key_dim] layout [K3-memory] §3 reports.
+ *   - q, k, v and out share one element type: KDA_DTYPE_F32 or KDA_DTYPE_BF16.
+ *     log_alpha, beta and states are always fp32.
+ *   - Every pointer is a device pointer to a dense row-major (contiguous)
+ *     array, 16-byte aligned (beta and cu_seqlens: 4-byte aligned, they are
+ *     read one element at a time).  The caller owns all memory; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  They return as soon as the work is queued.  Arguments are
+ *     validated on the host before any HIP call, so errors are reported
+ *     without touching the device.  Calls on different streams may run
+ *     concurrently if their outputs do not overlap.
+ *   - Supported now: d_k == d_v in {64, 128}.  Other valid sizes return
+ *     KDA_ERR_UNSUPPORTED.
+ *
+ * Numerics contract: log_alpha must be finite and, within each run of 16
+ * tokens that starts at a multiple of 16 from the sequence start, its sum per
+ * channel must stay above -80 (e.g. log_alpha >= -5 everywhere).  The chunked
+ * prefill relies on this to keep exp(-decay) within fp32 range; outside it,
+ * results may be inf/NaN.  NaN or Inf inputs propagate; they are not trapped.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* Element type of q, k, v and out. */
+enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
+
+/* Status codes (0 = success, negative = error). */
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* a size is negative or the sizes disagree */
+    KDA_ERR_UNSUPPORTED = -3, /* valid request this build does not implement */
+    KDA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented above */
+    KDA_ERR_ALIAS = -5,       /* an output overlaps an input it must not */
+    KDA_ERR_DEVICE = -6,      /* the current device is not a gfx950 GPU */
+    KDA_ERR_LAUNCH = -7       /* the kernel launch failed (hipGetLastError) */
+};
+
+/*
+ * kda_chunk_fwd -- prefill: the KDA recurrence over whole sequences, computed
+ * chunkwise ("recurrence between chunks, parallel work inside each chunk",
+ * [K3-explainer] §六.1) through the WY/UT representation of the chunk's
+ * rank-one updates ([K3-explainer] §六.2).  The result equals the token-by-
+ * token recurrence up to floating-point rounding; the chunk length (64) only
+ * affects speed.
+ *
+ * Layout (dense, cu_seqlens == NULL): B = batch sequences of T = seq_len
+ *   q, k       [B, T, H, d_k]   dtype
+ *   v, out     [B, T, H, d_v]   dtype
+ *   log_alpha  [B, T, H, d_k]   fp32
+ *   beta       [B, T, H]        fp32
+ *   initial_state, final_state  [B, H, d_v, d_k] fp32
+ * Layout (packed, cu_seqlens != NULL): batch must be 1, T = total tokens, and
+ *   N = num_seqs sequences are packed along T; sequence n covers tokens
+ *   [cu_seqlens[n], cu_seqlens[n+1]).  cu_seqlens is a DEVICE int32 array of
+ *   N + 1 entries with cu_seqlens[0] == 0, non-decreasing, cu_seqlens[N] == T.
+ *   States are [N, H, d_v, d_k].  The host cannot read cu_seqlens without a
+ *   sync, so its contents are not validated; the kernel clamps every offset to
+ *   [0, T] (malformed offsets give wrong results, never out-of-bounds access).
+ *
+ * initial_state == NULL means zero initial states.  final_state == NULL means
+ * the final states are not written.  final_state may be the same pointer as
+ * initial_state (in-place update); any other overlap between outputs and
+ * inputs returns KDA_ERR_ALIAS.  Empty sequences (and T == 0) are allowed:
+ * their final state is their initial state.
+ *
+ * Returns KDA_OK or a kda_status error code.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  void *out, float *final_state, int32_t batch, int32_t seq_len,
+                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
+                  int32_t dtype, hipStream_t stream);
+
+/*
+ * kda_decode_step -- one new token per session against a stored state: the
+ * fixed-size read and in-place update that decoding performs instead of
+ * appending to a cache ([K3-memory] §2; [Kimi-Linear], the decode discussion).
+ * In predict/correct form ([K3-explainer] §三, §四), per session b and head h:
+ *     S' = Diag(alpha) S,  e = v - S'^T k,  S <- S' + beta k e^T,  o = S^T q.
+ *
+ * Layout:
+ *   q, k       [B, H, d_k]   dtype
+ *   v, out     [B, H, d_v]   dtype
+ *   log_alpha  [B, H, d_k]   fp32
+ *   beta       [B, H]        fp32
+ *   state      [B, H, d_v, d_k] fp32, read and updated in place.
+ * out must not overlap any input or the state (KDA_ERR_ALIAS).  B == 0 is a
+ * no-op.  Returns KDA_OK or a kda_status error code.
+ */
+int kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                    const float *beta, float *state, void *out, int32_t batch,
+                    int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t dtype,
+                    hipStream_t stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *kda_status_string(int status);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,180 @@
+"""GPU parity of kda_chunk_fwd against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import TOL, compare_prefill, f64, max_rel_l2, say
+
+import gated_delta_rule_81_amd as kda
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run(inp, **kw):
+    d = to_dev(inp)
+    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                             d["initial_state"], d["cu_seqlens"], **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def check(inp, out, fin, seqs=None, heads=None, label=""):
+    e_out, e_st = compare_prefill(inp, out.cpu(), fin.cpu() if fin is not None else None,
+                                  seqs, heads)
+    tol = TOL[inp["q"].dtype]
+    print(f"{label}: out {e_out:.2e} state {e_st:.2e} (tol {tol})")
+    assert e_out <= tol and e_st <= tol, (e_out, e_st)
+
+
+# ---------------------------------------------------------------- small, exhaustive
+def test_tiny_fp32_workload():
+    """B=1 H=2 T=256 d=64 fp32, zero initial state, seed 0 (1e-4 bound)."""
+    inp = synth.prefill_inputs("tiny")
+    say("tiny fp32")
+    out, fin = run(inp)
+    check(inp, out, fin, label="tiny fp32")
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 200, 333])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_ragged_lengths(T, d):
+    """Several chunks and a ragged last chunk, nonzero initial state."""
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=T, heads=3, head_dim=d, batch=2)
+    say("bf16 ragged", T, d)
+    out, fin = run(inp)
+    check(inp, out, fin, label=f"bf16 T={T} d={d}")
+
+
+@pytest.mark.parametrize("T", [1, 63, 130])
+def test_fp32_ragged_with_state(T):
+    inp = synth.prefill_inputs("tiny", seq_len=T, heads=3, batch=2, init_std=0.02)
+    say("fp32 ragged", T)
+    out, fin = run(inp)
+    check(inp, out, fin, label=f"fp32 T={T}")
+
+
+def test_varlen_packed_small():
+    """Packed sequences including empty and one-token ones."""
+    lens = [0, 1, 63, 64, 65, 130, 7, 0, 200]
+    w = synth.WORKLOADS["varlen_16"]
+    parts = [synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=4, seed=100 + i)
+             for i, n in enumerate(lens)]
+    cat = lambda key: torch.cat([p[key] for p in parts], dim=1)
+    inp = {key: cat(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+    inp["initial_state"] = torch.cat([p["initial_state"] for p in parts])
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    say("varlen small", lens)
+    out, fin = run(inp)
+    check(inp, out, fin, label="varlen small")
+    # empty sequences return their initial state unchanged
+    for n in (0, 7):
+        assert torch.equal(fin[n].cpu(), inp["initial_state"][n])
+
+
+def test_strong_decay_gates():
+    """log_alpha = -5 everywhere (inside the numerics contract)."""
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=150, heads=2, head_dim=128)
+    inp["log_alpha"] = torch.full_like(inp["log_alpha"], -5.0)
+    say("strong decay")
+    out, fin = run(inp)
+    check(inp, out, fin, label="log_alpha=-5")
+
+
+def test_beta_zero_alpha_one_reads_frozen_state():
+    """beta = 0 and alpha = 1: o_t = S_0^T q_t and the state is unchanged."""
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=100, heads=2, head_dim=128)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    inp["log_alpha"] = torch.zeros_like(inp["log_alpha"])
+    say("beta=0 alpha=1")
+    out, fin = run(inp)
+    check(inp, out, fin, label="frozen")
+    assert max_rel_l2([(f64(fin.cpu()), f64(inp["initial_state"]))]) < 1e-6
+
+
+def test_split_resume_and_in_place_state():
+    """[0, t) then [t, T) from the first final state equals one pass; the second
+    call updates the state in place (final_state is initial_state)."""
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=300, heads=3, head_dim=128)
+    d = to_dev(inp)
+    say("split/resume")
+    full, fin_full = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                                   d["initial_state"])
+    t = 128  # chunk-aligned split: identical chunk boundaries, so bitwise equal
+    sl = lambda key, a, b: d[key][:, a:b].contiguous()
+    o1, s1 = kda.chunk_fwd(*(sl(key, 0, t) for key in ("q", "k", "v", "log_alpha", "beta")),
+                           d["initial_state"])
+    o2, s2 = kda.chunk_fwd(*(sl(key, t, 300) for key in ("q", "k", "v", "log_alpha", "beta")),
+                           s1, final_state=s1)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == s1.data_ptr()
+    assert torch.equal(torch.cat([o1, o2], dim=1), full)
+    assert torch.equal(s2, fin_full)
+
+
+def test_varlen_equals_separate_runs_and_is_deterministic():
+    lens = [100, 257, 64]
+    parts = [synth.prefill_inputs("k3_prefill_32k", seq_len=n, heads=2, head_dim=128,
+                                  seed=200 + i) for i, n in enumerate(lens)]
+    cat = lambda key: torch.cat([p[key] for p in parts], dim=1)
+    inp = {key: cat(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+    inp["initial_state"] = torch.cat([p["initial_state"] for p in parts])
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    say("varlen vs separate")
+    out, fin = run(inp)
+    out2, fin2 = run(inp)
+    assert torch.equal(out, out2) and torch.equal(fin, fin2)
+    off = 0
+    for i, p in enumerate(parts):
+        o, f = run(p)
+        assert torch.equal(o[0], out[0, off:off + lens[i]])
+        assert torch.equal(f[0], fin[i])
+        off += lens[i]
+
+
+def test_no_initial_state_equals_zeros_and_no_final_state():
+    inp = synth.prefill_inputs("prefill_4k", seq_len=90, heads=2)
+    say("null states")
+    d = to_dev(inp)
+    o1, f1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None)
+    zeros = torch.zeros_like(f1)
+    o2, f2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], zeros)
+    o3, f3 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], None,
+                           output_final_state=False)
+    torch.cuda.synchronize()
+    assert f3 is None
+    assert torch.equal(o1, o2) and torch.equal(f1, f2) and torch.equal(o1, o3)
+
+
+# ---------------------------------------------------------------- workloads
+def test_prefill_4k_workload_full():
+    """B=1 H=32 T=4096 d=128 bf16, zero state: every head checked."""
+    inp = synth.prefill_inputs("prefill_4k")
+    say("prefill_4k full")
+    out, fin = run(inp)
+    check(inp, out, fin, label="prefill_4k")
+
+
+def test_k3_prefill_32k_workload_sampled_heads():
+    """B=1 H=96 T=32768 d=128 bf16, state N(0, 0.02): the full launch, with four
+    heads (first, last, two inner) checked over the whole sequence."""
+    inp = synth.prefill_inputs("k3_prefill_32k")
+    say("k3_prefill_32k full launch")
+    out, fin = run(inp)
+    check(inp, out, fin, heads=[0, 37, 64, 95], label="k3_prefill_32k")
+
+
+def test_varlen_16_workload_sampled():
+    """16 packed sequences (U[1024, 65536] tokens), H=32: the full launch, with the
+    shortest and the longest sequence checked on two heads each."""
+    inp = synth.prefill_inputs("varlen_16")
+    lens = np.diff(inp["cu_seqlens"].numpy())
+    say("varlen_16 full launch", int(lens.sum()), "tokens")
+    out, fin = run(inp)
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
+    check(inp, out, fin, seqs=seqs, heads=[0, 31], label="varlen_16")
