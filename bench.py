@@ -1,0 +1,237 @@
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = the whole hot path once:
+  * kda_chunk_fwd over the K3-shaped prefill (B=1, H=96, T=32768, d=128,
+    bf16 q/k/v, fp32 gates and state, state ~ N(0, 0.02)), and
+  * one kda_decode_step of the batched decode workload (B=256 sessions, H=96,
+    d=128, fp32 state [256, 96, 128, 128] ~ N(0, 0.02)); step s uses token
+    s mod 64 of the workload's 64 sequential tokens and updates the state in
+    place, so consecutive steps are consecutive decode tokens.
+
+Inputs are seeded synthetic data resident in HBM before timing starts.  Each
+kernel is bracketed by HIP events on the stream it runs on (torch's current
+stream), so the per-kernel averages are kernel time only.
+
+Output: one JSON line (rank 0).  ``value`` is prefill tokens/s
+(B*T / mean kda_chunk_fwd time); the decode figure (state-update GB/s) is in
+``decode``; ``ms_per_step`` is the wall time per step (both kernels).
+``roofline`` is for kda_chunk_fwd and ``decode.roofline`` for the decode
+kernel, both against HBM (8 TB/s).  ``cpu_baseline`` is the fp64 oracle on
+the host cores over a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--copy-calibration]   (adds a 1 GiB device copy after timing, used to
+                               scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+PREFILL_FLOP_PER_TOKEN_HEAD = 140629  # d=128, C=64, triangular products
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(T_tokens, H, d, n_seqs, esz=2):
+    """Algorithmic HBM bytes of one kda_chunk_fwd: read q, k, v (esz each),
+    log_alpha (fp32), beta (fp32), the initial state; write out (esz) and the
+    final state."""
+    per_token_head = 3 * d * esz + 4 * d + 4 + d * esz
+    return T_tokens * H * per_token_head + 2 * n_seqs * H * d * d * 4
+
+
+def decode_bytes(B, H, d, esz=2):
+    """Algorithmic HBM bytes of one kda_decode_step: the fp32 state read and
+    written once, plus q, k, v, log_alpha, beta in and out."""
+    return B * H * (2 * d * d * 4 + 3 * d * esz + 4 * d + 4 + d * esz)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in ("kda_chunk.hip", "kda_device.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per kda_chunk_fwd launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha256") != source_digest():
+        return None
+    return doc.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, heads, threads):
+    """The fp64 oracle on `heads` heads of the prefill workload over its full
+    length, on the host cores; scaled to tokens/s of the whole workload."""
+    import numpy as np
+    import oracle
+
+    H = inp["q"].shape[2]
+    f = lambda key: inp[key][0, :, :heads].float().numpy().astype(np.float64)
+    q, k, v, g = (f(key) for key in ("q", "k", "v", "log_alpha"))
+    b = inp["beta"][0, :, :heads].numpy().astype(np.float64)
+    s0 = inp["initial_state"][:, :heads].numpy().astype(np.float64)
+    T = q.shape[0]
+    t0 = time.perf_counter()
+    oracle.kda_forward(q, k, v, g, b, state0=s0, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": T * heads / dt / H, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {H} heads x {T} tokens of the prefill workload, "
+                      f"fp64, {dt:.1f} s; value = sample token-heads/s / {H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=96)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import gated_delta_rule_81_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w_pre = synth.WORKLOADS["k3_prefill_32k"]
+    w_dec = synth.WORKLOADS["decode_b256"]
+
+    log("generating", w_pre.notes)
+    pre = synth.prefill_inputs(w_pre)
+    log("generating", w_dec.notes)
+    dec = synth.decode_inputs(w_dec)
+    P = {key: pre[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
+    Dn = {key: dec[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
+    state = dec["state"].to(dev)
+    out = torch.empty_like(P["v"])
+    fin = torch.empty_like(P["initial_state"])
+    dout = torch.empty((w_dec.batch, w_dec.heads, w_dec.head_dim), dtype=torch.bfloat16,
+                       device=dev)
+    torch.cuda.synchronize()
+
+    def step(s):
+        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["initial_state"],
+                      out=out, final_state=fin)
+        t = s % w_dec.steps
+        kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
+                        state, out=dout)
+
+    log(f"warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    stream = torch.cuda.current_stream(dev)
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["initial_state"],
+                      out=out, final_state=fin)
+        e[1].record(stream)
+        t = (args.warmup + s) % w_dec.steps
+        kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
+                        state, out=dout)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sorted(ev[s][0].elapsed_time(ev[s][1]) for s in range(K))
+    dec_ms = sorted(ev[s][1].elapsed_time(ev[s][2]) for s in range(K))
+    pre_avg = sum(pre_ms) / K
+    dec_avg = sum(dec_ms) / K
+    log(f"chunk_fwd avg {pre_avg:.4f} ms (min {pre_ms[0]:.4f}, median {pre_ms[K // 2]:.4f}); "
+        f"decode_step avg {dec_avg:.4f} ms (min {dec_ms[0]:.4f})")
+
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copies")
+
+    T_tok = w_pre.batch * w_pre.seq_len
+    pbytes = prefill_bytes(T_tok, w_pre.heads, w_pre.head_dim, w_pre.batch)
+    dbytes = decode_bytes(w_dec.batch, w_dec.heads, w_dec.head_dim)
+    pre_gbs = pbytes / (pre_avg * 1e-3) / 1e9
+    dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
+    pre_tflops = PREFILL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    result = {
+        "metric": "KDA chunked-fwd tokens/s (H=96,d=128,T=32K); decode state-update HBM GB/s",
+        "value": T_tok / (pre_avg * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_chunk_fwd B=1 H=96 T=32768 d_k=d_v=128 bf16 q/k/v, "
+                               "fp32 gates/state, chunk 64 + kda_decode_step B=256 H=96 d=128",
+                   "prefill_tokens": T_tok, "heads": w_pre.heads, "head_dim": w_pre.head_dim,
+                   "decode_sessions": w_dec.batch},
+        "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pre_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "prefill": {"kernel_ms_avg": pre_avg, "kernel_ms_min": pre_ms[0],
+                    "kernel_ms_median": pre_ms[K // 2], "algorithmic_bytes": pbytes,
+                    "mfma_bf16_tflops_algorithmic": pre_tflops,
+                    "mfma_frac_algorithmic": pre_tflops / BF16_DENSE_PEAK_TFLOPS},
+        "decode": {"metric": "decode state-update HBM GB/s", "value": dec_gbs, "unit": "GB/s",
+                   "kernel_ms_avg": dec_avg, "kernel_ms_min": dec_ms[0],
+                   "algorithmic_bytes": dbytes, "tokens_per_s": w_dec.batch / (dec_avg * 1e-3),
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                                "traffic": None}},
+    }
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        threads = max(1, min(threads, 16))
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads, {threads} threads")
+        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads, threads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
