@@ -20,8 +20,10 @@ kernel, both against HBM (8 TB/s).  ``cpu_baseline`` is the fp64 oracle on
 the host cores over a bounded sample of the prefill workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--copy-calibration]   (adds a 1 GiB device copy after timing, used to
+       [--copy-calibration]   (adds 1 GiB device copies after timing, used to
                                scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+       [--skip-decode]        (decode workload shrunk to one session-head; for
+                               counter passes on kda_chunk_fwd only)
 """
 from __future__ import annotations
 
@@ -109,6 +111,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true",
+                    help="time kda_chunk_fwd only (for counter passes); no decode fields")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
@@ -127,6 +131,8 @@ def main():
 
     log("generating", w_pre.notes)
     pre = synth.prefill_inputs(w_pre)
+    if args.skip_decode:
+        w_dec = synth.replace(w_dec, batch=1, heads=1, steps=1)
     log("generating", w_dec.notes)
     dec = synth.decode_inputs(w_dec)
     P = {key: pre[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta", "initial_state")}

@@ -23,6 +23,8 @@ typedef __bf16 bf16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -80,6 +82,17 @@ __device__ __forceinline__ void store8(bf16 *p, const float (&f)[8]) {
 __device__ __forceinline__ void store8(float *p, const float (&f)[8]) {
     *reinterpret_cast<f32x4 *>(p) = f32x4{f[0], f[1], f[2], f[3]};
     *reinterpret_cast<f32x4 *>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
+// Store two floats as two consecutive T.
+__device__ __forceinline__ void store2(bf16 *p, float a, float b) {
+    bf16x2 v;
+    v[0] = static_cast<bf16>(a);
+    v[1] = static_cast<bf16>(b);
+    *reinterpret_cast<bf16x2 *>(p) = v;
+}
+__device__ __forceinline__ void store2(float *p, float a, float b) {
+    *reinterpret_cast<f32x2 *>(p) = f32x2{a, b};
 }
 
 // Store four floats as four consecutive T.

@@ -28,7 +28,7 @@ from dataclasses import dataclass, field, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "prefill_inputs", "decode_inputs",
-           "sequence_inputs", "varlen_lengths"]
+           "sequence_inputs", "varlen_lengths", "replace"]
 
 
 @dataclass(frozen=True)

@@ -178,3 +178,25 @@ def test_varlen_16_workload_sampled():
     out, fin = run(inp)
     seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
     check(inp, out, fin, seqs=seqs, heads=[0, 31], label="varlen_16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mixed_strong_decay_chunks(d):
+    """A burst of strong decay in the second chunk and in the ragged last chunk
+    (a few channels at log_alpha = -4.9): those chunks take the 16-token-window
+    path, the others the single-pass path; both must match the oracle."""
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=300, heads=2, head_dim=d)
+    g = inp["log_alpha"]
+    g[:, 64:128, :, :5] = -4.9
+    g[:, 260:300, :, 7:9] = -4.9
+    say("mixed strong decay", d)
+    out, fin = run(inp)
+    check(inp, out, fin, label=f"mixed decay d={d}")
+
+
+def test_fp32_strong_decay_windowed():
+    inp = synth.prefill_inputs("tiny", seq_len=150, heads=2)
+    inp["log_alpha"] = torch.full_like(inp["log_alpha"], -3.0)
+    say("fp32 strong decay")
+    out, fin = run(inp)
+    check(inp, out, fin, label="fp32 log_alpha=-3")
