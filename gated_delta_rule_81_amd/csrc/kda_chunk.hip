@@ -136,44 +136,96 @@ struct ChunkRegs {
     float beta;
 };
 
-// Rows r of the chunk starting at token tok0 with lo <= r < hi and r < nvalid
-// are loaded; every other row reads as zero (a zero row is an inert token).
+// Buffer descriptors for one chunk: the base points at the chunk's first
+// token and the size covers exactly its nvalid tokens, so every load of a row
+// at or beyond nvalid returns zeros (an inert token) without a branch.
+struct ChunkSrc {
+    __amdgpu_buffer_rsrc_t k, q, g, v, b;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+template <typename T>
+__device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v,
+                                              const float *log_alpha, const float *beta,
+                                              int64_t tok0, int nvalid, int H, int D) {
+    const int64_t e0 = tok0 * H * D;
+    const int bytes = nvalid * H * D;  // elements; callers keep H * D * 64 * 4 < 2^31
+    ChunkSrc s;
+    s.k = __builtin_amdgcn_make_buffer_rsrc((void *)(k + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
+    s.q = __builtin_amdgcn_make_buffer_rsrc((void *)(q + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
+    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
+    s.g = __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, bytes * 4, kRsrcWord3);
+    s.b = __builtin_amdgcn_make_buffer_rsrc((void *)(beta + tok0 * H), 0, nvalid * H * 4,
+                                            kRsrcWord3);
+    return s;
+}
+
+template <typename T> __device__ __forceinline__ typename Vec8<T>::raw buf8(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ u32x4 buf8<bf16>(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ f32x8 buf8<float>(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+    return f32x8{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                 __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
+                 __uint_as_float(b[2]), __uint_as_float(b[3])};
+}
+__device__ __forceinline__ f32x4 buf4f(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return f32x4{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                 __uint_as_float(a[3])};
+}
+
+// Byte offsets (relative to a chunk's first token) of this thread's loads;
+// loop-invariant, so the chunk loop only rebuilds the scalar descriptors.
 template <typename T, int D, int DVS>
-__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS> &R, const T *__restrict__ q,
-                                           const T *__restrict__ k, const T *__restrict__ v,
-                                           const float *__restrict__ log_alpha,
-                                           const float *__restrict__ beta, int64_t tok0,
-                                           int nvalid, int lo, int hi, int h, int H, int v0,
-                                           int tid) {
+struct ChunkOffsets {
     typedef Cfg<T, D, DVS> G;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int I = wave >> 1, cb = (wave & 1) * (D / 2);
-    const int rg = lane % G::RGB, cg = lane / G::RGB;
-    const int c0 = cb + 8 * cg;
-    const int end = nvalid < hi ? nvalid : hi;
+    int kq[G::RPT], g[G::RPT], v, b;
+    __device__ ChunkOffsets(int tid, int h, int H, int v0) {
+        const int lane = tid & 63, wave = tid >> 6;
+        const int I = wave >> 1, cb = (wave & 1) * (D / 2);
+        const int rg = lane % G::RGB, cg = lane / G::RGB;
+        const int c0 = cb + 8 * cg;
 #pragma unroll
-    for (int j = 0; j < G::RPT; ++j) {
-        const int r = kBS * I + G::RPT * rg + j;
-        if (r >= lo && r < end) {
-            const int64_t off = ((tok0 + r) * H + h) * (int64_t)D + c0;
-            R.k[j] = load8(k + off);
-            R.q[j] = load8(q + off);
-            R.g[j][0] = *reinterpret_cast<const f32x4 *>(log_alpha + off);
-            R.g[j][1] = *reinterpret_cast<const f32x4 *>(log_alpha + off + 4);
-        } else {
-            R.k[j] = Vec8<T>::zero();
-            R.q[j] = Vec8<T>::zero();
-            R.g[j][0] = zero4();
-            R.g[j][1] = zero4();
+        for (int j = 0; j < G::RPT; ++j) {
+            const int r = kBS * I + G::RPT * rg + j;
+            kq[j] = ((r * H + h) * D + c0) * (int)sizeof(T);
+            g[j] = ((r * H + h) * D + c0) * 4;
         }
-    }
-    R.v = Vec8<T>::zero();
-    if (tid < G::VTH) {
         const int vr = tid / (DVS / 8), vc = 8 * (tid % (DVS / 8));
-        if (vr >= lo && vr < end)
-            R.v = load8(v + ((tok0 + vr) * H + h) * (int64_t)D + v0 + vc);
+        v = ((vr * H + h) * D + v0 + vc) * (int)sizeof(T);
+        b = (tid * H + h) * 4;
     }
-    R.beta = (tid >= lo && tid < end) ? beta[(tok0 + tid) * H + h] : 0.f;
+};
+
+// The next chunk's registers are loaded in three parts, issued in different
+// phases so the vector memory unit drains them in the background.
+template <typename T, int D, int DVS>
+__device__ __forceinline__ void load_kq(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
+                                        const ChunkOffsets<T, D, DVS> &o) {
+#pragma unroll
+    for (int j = 0; j < Cfg<T, D, DVS>::RPT; ++j) {
+        R.k[j] = buf8<T>(s.k, o.kq[j]);
+        R.q[j] = buf8<T>(s.q, o.kq[j]);
+    }
+}
+template <typename T, int D, int DVS>
+__device__ __forceinline__ void load_g(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
+                                       const ChunkOffsets<T, D, DVS> &o) {
+#pragma unroll
+    for (int j = 0; j < Cfg<T, D, DVS>::RPT; ++j) {
+        R.g[j][0] = buf4f(s.g, o.g[j]);
+        R.g[j][1] = buf4f(s.g, o.g[j] + 16);
+    }
+}
+template <typename T, int D, int DVS>
+__device__ __forceinline__ void load_vb(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
+                                        const ChunkOffsets<T, D, DVS> &o, int tid) {
+    R.v = tid < Cfg<T, D, DVS>::VTH ? buf8<T>(s.v, o.v) : Vec8<T>::zero();
+    R.beta = tid < kC ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.b, o.b, 0, 0)) : 0.f;
 }
 
 template <typename T, int D, int DVS>
@@ -267,17 +319,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int prg = lane % G::RGB, pcg = lane / G::RGB;
     const int pc0 = (wave & 1) * (D / 2) + 8 * pcg;
 
+    const ChunkOffsets<T, D, DVS> offs(tid, h, H, v0);
     ChunkRegs<T, D, DVS> R;
-    if (nchunks > 0)
-        load_chunk<T, D, DVS>(R, q, k, v, log_alpha, beta, tbeg,
-                              (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), 0, kC, h, H, v0,
-                              tid);
+    if (nchunks > 0) {
+        const ChunkSrc s0 = chunk_src(q, k, v, log_alpha, beta, tbeg,
+                                      (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D);
+        load_kq(R, s0, offs);
+        load_g(R, s0, offs);
+        load_vb(R, s0, offs, tid);
+    }
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int64_t tok0 = tbeg + (int64_t)ch * kC;
         const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
         const int64_t ntok0 = tok0 + kC;
         const int nnext = ch + 1 < nchunks ? (int)((tend - ntok0) < kC ? (tend - ntok0) : kC) : 0;
+        const ChunkSrc nsrc = chunk_src(q, k, v, log_alpha, beta, ntok0, nnext, H, D);
 
         int npass = 1;  // 4 when the chunk is redone as 16-token windows
         for (int pass = 0; pass < npass; ++pass) {
@@ -440,9 +497,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             }
             // Prefetch the next chunk's inputs once this chunk's last pass has
             // consumed the registers; they arrive while the chunk is computed.
-            if (pass == npass - 1 && nnext > 0)
-                load_chunk<T, D, DVS>(R, q, k, v, log_alpha, beta, ntok0, nnext, 0, kC, h, H,
-                                      v0, tid);
+            const bool prefetch = pass == npass - 1 && nnext > 0;
+            if (prefetch) load_kq(R, nsrc, offs);
 
             // -------------------------------------------------------- A, Mqk
 #pragma unroll
@@ -477,6 +533,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 }
             }
             __syncthreads();
+
+            if (prefetch) load_g(R, nsrc, offs);
 
             // ------------------------------------- T diagonal || [K+; Q+] S
             f32x4 PQ[G::NCT];
@@ -552,6 +610,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 }
             }
             __syncthreads();
+
+            if (prefetch) load_vb(R, nsrc, offs, tid);
 
             // Off-diagonal blocks: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ, level by level.
 #pragma unroll
