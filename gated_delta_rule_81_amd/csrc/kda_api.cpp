@@ -91,6 +91,8 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_
     const int d = head_dim_k;
     if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
     if (dtype == kda::kDtypeF32 && d != 64) return KDA_ERR_UNSUPPORTED;
+    // the kernel addresses 64 tokens of one tensor with 32-bit byte offsets
+    if ((int64_t)num_heads * d * 4 * 64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     // alignment
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
         !aligned4(beta) || !aligned16(initial_state) || !aligned16(out) ||

@@ -6,7 +6,7 @@
 //   [K3-memory]     "Kimi K3 Changed the Memory Math for Agentic AI Forever".
 //
 // The recurrence S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,
-// o_t = S_t^T q_t ([K3-explainer] §四, §二.1) is evaluated per chunk of C = 64
+// o_t = S_t^T q_t ([K3-explainer] §四, §二.1) is evaluated per chunk of C = 32
 // tokens: state recurrence between chunks, dense products inside a chunk
 // ([K3-explainer] §六.1), with the chunk's rank-one erase/write products
 // gathered into a few matrices ([K3-explainer] §六.2, WY representation).
@@ -15,33 +15,46 @@
 // log-decay Gamma_r = sum_{s<=r} log a_s (reset each chunk):
 //
 //   K+ = K (.) e^Gamma,  Q+ = Q (.) e^Gamma,  K- = K (.) e^-Gamma
-//   A       = StrictTril(diag(b) K+ K-^T),  T = (I + A)^{-1}
+//   A       = StrictTril(diag(b) K+ K-^T),  T = (I + A)^{-1},  T' = T diag(b)
 //   X       = V - K+ S                        (prediction error against S)
-//   Delta   = T diag(b) X                     (the chunk's corrected writes)
+//   Delta   = T' X                            (the chunk's corrected writes)
 //   O       = Q+ S + Tril(Q+ K-^T) Delta
 //   S_next  = Diag(e^{Gamma_last}) S + (K (.) e^{Gamma_last - Gamma})^T Delta
 //
 // The chunk transition S -> S_next is the page's "P = D - K W^T" form
 // ([K3-explainer] §六.2) with D = Diag(e^{Gamma_last}).
 //
-// Range of the factors.  e^Gamma <= 1 but e^-Gamma grows with the decay
-// accumulated inside the chunk.  A chunk whose |Gamma| (log2 units) reaches
-// 120 anywhere is recomputed as four 16-token windows, each a chunk of its own
-// (rows outside the window are zero); inside 16 tokens the factors stay in
-// range as long as 16 consecutive log-gates sum to more than -80 per channel.
+// Range of the factors.  The products inside a chunk only need
+// e^{Gamma_i - Gamma_j} for j <= i, which is <= 1, but e^{-Gamma} alone grows
+// with the decay accumulated since its reference point.  The chunk is two
+// 16-token blocks; block 0 is referenced to the chunk start and block 1 to
+// its own start rho = Gamma_15:
+//   * K+, Q+ (chunk-relative, <= |k|, |q|) feed [K+; Q+] S and the block
+//     (1,0) tiles; K- of block 0 (chunk-relative) feeds tiles (0,0), (1,0);
+//   * the diagonal tile (1,1) uses K+, Q+, K- of block 1 relative to rho.
+// Every factor is then bounded by e^{decay over 16 tokens}, so the numerics
+// contract (16-token decay sum > -80 per channel) keeps all of them finite.
+// K_end = K (.) e^{Gamma_last - Gamma} is formed as (K e^{rho - Gamma})
+// e^{Gamma_last - rho}, two factors in fp32 range.
 //
-// Work split inside a workgroup (8 waves, 512 threads), per chunk:
-//   prep   : cumulative log-decay per 16-token block (DPP lane scan) plus
-//            block offsets, e^{+-Gamma} (v_exp_f32), operand tiles in LDS;
-//   A, Mqk : 20 MFMA tiles of 16x16 (lower triangle only);
-//   T      : diagonal 16x16 blocks by right-looking substitution on one wave
-//            while waves 4-7 compute [K+; Q+] S; then the off-diagonal blocks
-//            in three dependency levels (MFMA);
-//   scan   : Delta = T' X, O = Q+ S + Mqk Delta, and S <- gamma S + Kend^T
-//            Delta with the fp32 master state held in MFMA accumulators
-//            across chunks; a bf16 (or fp32) shadow copy of S in LDS feeds the
-//            next chunk's products.
-// Inputs for chunk n+1 are loaded into registers while chunk n is computed.
+// Work split inside a workgroup.  D/16 preparation waves and DVS/16 scan
+// waves run in lockstep, three workgroup barriers per chunk: while the
+// preparation waves build chunk n+1's operands, each scan wave advances its
+// 16 value columns of the state over chunk n.  Prepared operands are double
+// buffered in LDS.
+//   preparation, phase 1: cumulative log-decay (DPP lane scan), e^{+-Gamma}
+//                (v_exp_f32), operand tiles in LDS, next chunk's loads;
+//                phase 2: A and Tril(Q+ K-^T) (6 MFMA tiles), the diagonal
+//                blocks of T = (I + A)^{-1} by substitution;
+//                phase 3: the off-diagonal block of T (two MFMA products).
+//   scan, phase 1: [K+; Q+] S, X, Delta = T' X, O (stored);
+//         phase 2: S <- gamma S + Kend^T Delta.
+// A scan wave keeps its state columns (all d_k rows) in fp32 MFMA
+// accumulators and feeds them straight back as the B operand of the next
+// chunk's products: the contraction index is permuted so that the
+// accumulator layout is the operand layout (see `phys`), and the operand
+// tiles in LDS are stored in that permuted order.  X, Delta and O stay in
+// registers the same way.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -49,96 +62,72 @@ namespace kda {
 
 namespace {
 
-constexpr int kC = 64;              // chunk length
-constexpr int kBS = 16;             // tile / sub-block size
-constexpr int kNB = kC / kBS;       // sub-blocks per chunk
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr float kMaxLog2Decay = 120.f;  // |Gamma| bound of the single-pass chunk
+constexpr int kC = 32;   // chunk length
+constexpr int kBS = 16;  // block / tile size
 
-// (I, J) of the lower-triangular 16x16 tiles, J <= I, row-major order.
-__device__ __forceinline__ void tile_ij(int t, int &I, int &J) {
-    I = (t >= 1) + (t >= 3) + (t >= 6);
-    J = t - I * (I + 1) / 2;
+// Physical position of contraction index i (a key channel or a token) in
+// the LDS operand tiles.  For bf16 the 16x16x32 MFMA reads, in lane group
+// g = lane / 16, 8 consecutive physical entries; they hold the logical
+// indices {4g .. 4g+3, 16 + 4g .. 16 + 4g + 3} of each group of 32, which are
+// exactly the rows that lane holds of two stacked 16x16 accumulator tiles.
+// fp32 (16x16x4 MFMA, one index per lane per step) keeps the natural order.
+template <typename T>
+__device__ __forceinline__ int phys(int i) {
+    if constexpr (sizeof(T) == 2) {
+        const int j = i & 31;
+        return (i & ~31) + 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+    } else {
+        return i;
+    }
 }
-
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
-// K_end^T is stored [key channel][token] with the token index XOR-swizzled by
-// a multiple of 16 per channel group: the prep's transposed stores (8 channel
-// groups x 8 token pairs per wave) and the MFMA reads (16 channels x 4 runs of
-// 8 tokens) then both spread over all 64 LDS banks.  Runs of 8 tokens stay
-// contiguous and inside [0, 64).
-__device__ __forceinline__ int kend_col(int c, int t) { return t ^ (8 * ((c >> 3) & 6)); }
 
 template <typename T, int D, int DVS>
 struct Cfg {
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int kPad = 16 / SZ;
-    static constexpr int LDK = D + kPad;     // [C][D] tiles
-    static constexpr int LDC = kC + kPad;    // [*][C] tiles
-    static constexpr int LDA = kC + 4;       // fp32 A
+    static constexpr int PW = D / 16;        // preparation waves
+    static constexpr int SWV = DVS / 16;     // scan waves (one per 16 value columns)
+    static constexpr int THREADS = 64 * (PW + SWV);
+    static constexpr int LDK = D + kPad;     // [token][channel] tiles
+    static constexpr int LDT = kC + kPad;    // [*][token] tiles
+    static constexpr int LDV = DVS + kPad;   // V slice rows
+    static constexpr int LDO = 16 + kPad;    // O staging rows (per scan wave)
     static constexpr int LDAT = kBS + 4;     // fp32 transposed diagonal blocks of A
-    static constexpr int LDV = DVS + kPad;   // V slice
-    static constexpr int LDD = kBS + kPad;   // diagonal T blocks
-    static constexpr int TDB = kBS * LDD + kPad;  // stride between diagonal blocks
-    static constexpr int LDX = kBS + 4;      // fp32 scratch
-    static constexpr int NCT = DVS / 16;     // d_v column tiles
+    static constexpr int LDTT = kBS + kPad;  // 16x16 operand blocks of the substitution
     static constexpr int NRT = D / 16;       // d_k row tiles of the state
-    static constexpr int RPT = D / 64;       // prep: rows per thread
-    static constexpr int RGB = kBS / RPT;    // prep: row groups per 16-row block
-    static constexpr int VTH = kC * DVS / 8; // threads that move the V and O slices
+    static constexpr int KB = sizeof(T) == 2 ? 32 : 16;  // contraction block per operand fragment
+    static constexpr int VE = 16 / SZ;       // elements per 16-byte V access
+    static constexpr int VTH = kC * DVS / VE;  // preparation threads that move the V slice
+    static constexpr int RW = 4 * SZ / 4;    // words per 4-channel run of k / q
 
-    static constexpr int TILE = kC * LDK * SZ;
-    static constexpr int XB = DVS * LDC * SZ;       // X (and Delta) transposed
-    static constexpr int SCRB = 3 * kBS * LDX * 4;  // fp32 T-level scratch
-    static constexpr int LDO = DVS + kPad;          // O staging rows (padded)
-    static constexpr int OB = kC * LDO * SZ;        // O staging
-    static constexpr int RKM = cmax(TILE, XB + cmax(SCRB, OB));
-    static constexpr int AB = kC * LDA * 4;
-
-    // byte offsets; K- region later holds X, scratch and O, the A region Delta
-    static constexpr int oKP = 0, oQP = TILE, oKM = 2 * TILE;
-    static constexpr int oX = oKM, oScr = oKM + XB, oO = oKM + XB;
-    static constexpr int oA = oKM + RKM, oDL = oA;
-    static constexpr int oAt = oA + AB;
-    static constexpr int oKendT = oAt + kNB * kBS * LDAT * 4;
-    static constexpr int oMqk = oKendT + D * LDC * SZ;
-    static constexpr int oTr = oMqk + kC * LDC * SZ;
-    static constexpr int oTt = oTr + kC * LDC * SZ;
-    static constexpr int oTd = oTt + kC * LDC * SZ;
-    static constexpr int oS = oTd + kNB * TDB * SZ;
-    static constexpr int oV = oS + DVS * LDK * SZ;
-    static constexpr int oBeta = oV + kC * LDV * SZ;
-    static constexpr int oTot = oBeta + kC * 4;
-    static constexpr int oGam = oTot + kNB * D * 4;
-    static constexpr int oFlag = oGam + D * 4;
-    static constexpr int BYTES = oFlag + kWaves * 4;
+    // one buffer set of prepared operands (byte offsets inside the set)
+    static constexpr int B_TK = kC * LDK * SZ;
+    static constexpr int B_TT = kC * LDT * SZ;
+    // T3: T'_00 = T_00 diag(b_0), A_10, T_11 (16x16 each, row-major)
+    static constexpr int B_T16 = kBS * LDTT * SZ;
+    static constexpr int sKP = 0, sQP = B_TK, sKET = 2 * B_TK, sMQ = sKET + D * LDT * SZ,
+                         sT3 = sMQ + B_TT, sV = sT3 + 3 * B_T16, sGam = sV + kC * LDV * SZ,
+                         sF1 = sGam + D * 4, sBeta = sF1 + D * 4, SET = sBeta + kC * 4;
+    // preparation scratch
+    static constexpr int oKD = 2 * SET, oQD = oKD + kBS * LDK * SZ, oKM = oQD + kBS * LDK * SZ,
+                         oAt = oKM + B_TK;
+    // scan scratch: O staging, one region per scan wave
+    static constexpr int oO = oAt + 2 * kBS * LDAT * 4, BYTES = oO + SWV * kC * LDO * SZ;
 
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(DVS % 16 == 0 && D % DVS == 0, "d_v slice");
-    static_assert(VTH <= kThreads && VTH >= kC, "V slice map");
-    static_assert(2 * (64 / RGB) * 8 == D, "prep: two waves cover the channels of a block");
-    static_assert(XB <= AB, "Delta fits in the A region");
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(TILE % 16 == 0 && RKM % 16 == 0 && XB % 16 == 0 && oS % 16 == 0 &&
-                      oV % 16 == 0 && oTd % 16 == 0 && oMqk % 16 == 0 && oKendT % 16 == 0,
+    static_assert(VTH <= PW * 64 && VTH >= kC, "V slice map");
+    static_assert(D % KB == 0, "state contraction blocks");
+    static_assert(SET % 16 == 0 && oKM % 16 == 0 && oAt % 16 == 0 && oO % 16 == 0,
                   "16-byte alignment");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Registers holding one chunk's raw inputs (loaded one chunk ahead).
-template <typename T, int D, int DVS>
-struct ChunkRegs {
-    typedef Cfg<T, D, DVS> G;
-    typename Vec8<T>::raw k[G::RPT], q[G::RPT];
-    f32x4 g[G::RPT][2];
-    typename Vec8<T>::raw v;
-    float beta;
-};
-
+// --------------------------------------------------------------- raw loads
 // Buffer descriptors for one chunk: the base points at the chunk's first
 // token and the size covers exactly its nvalid tokens, so every load of a row
-// at or beyond nvalid returns zeros (an inert token) without a branch.
+// at or beyond nvalid returns zeros (an inert token: k = q = v = 0, a = 1,
+// b = 0) without a branch.
 struct ChunkSrc {
     __amdgpu_buffer_rsrc_t k, q, g, v, b;
 };
@@ -150,86 +139,194 @@ __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v
                                               const float *log_alpha, const float *beta,
                                               int64_t tok0, int nvalid, int H, int D) {
     const int64_t e0 = tok0 * H * D;
-    const int bytes = nvalid * H * D;  // elements; callers keep H * D * 64 * 4 < 2^31
+    const int elems = nvalid * H * D;  // the host keeps 64 * H * D * 4 < 2^31
     ChunkSrc s;
-    s.k = __builtin_amdgcn_make_buffer_rsrc((void *)(k + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
-    s.q = __builtin_amdgcn_make_buffer_rsrc((void *)(q + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
-    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, bytes * (int)sizeof(T), kRsrcWord3);
-    s.g = __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, bytes * 4, kRsrcWord3);
+    s.k = __builtin_amdgcn_make_buffer_rsrc((void *)(k + e0), 0, elems * (int)sizeof(T),
+                                            kRsrcWord3);
+    s.q = __builtin_amdgcn_make_buffer_rsrc((void *)(q + e0), 0, elems * (int)sizeof(T),
+                                            kRsrcWord3);
+    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, elems * (int)sizeof(T),
+                                            kRsrcWord3);
+    s.g = __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, elems * 4, kRsrcWord3);
     s.b = __builtin_amdgcn_make_buffer_rsrc((void *)(beta + tok0 * H), 0, nvalid * H * 4,
                                             kRsrcWord3);
     return s;
 }
 
-template <typename T> __device__ __forceinline__ typename Vec8<T>::raw buf8(__amdgpu_buffer_rsrc_t r, int off);
-template <> __device__ __forceinline__ u32x4 buf8<bf16>(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-template <> __device__ __forceinline__ f32x8 buf8<float>(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
-    return f32x8{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
-                 __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
-                 __uint_as_float(b[2]), __uint_as_float(b[3])};
-}
-__device__ __forceinline__ f32x4 buf4f(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return f32x4{__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
-                 __uint_as_float(a[3])};
+template <int NW> struct Raw { unsigned w[NW]; };
+
+template <int NW>
+__device__ __forceinline__ Raw<NW> buf_load(__amdgpu_buffer_rsrc_t r, int off) {
+    Raw<NW> x;
+    if constexpr (NW == 1) {
+        x.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (NW == 2) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        x.w[0] = a[0];
+        x.w[1] = a[1];
+    } else {
+        static_assert(NW == 4, "access width");
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x.w[i] = a[i];
+    }
+    return x;
 }
 
-// Byte offsets (relative to a chunk's first token) of this thread's loads;
-// loop-invariant, so the chunk loop only rebuilds the scalar descriptors.
+// N elements of T held in raw words -> floats.
+template <typename T, int N, int NW>
+__device__ __forceinline__ void unpack(const Raw<NW> &x, float *f) {
+    if constexpr (sizeof(T) == 2) {
+        static_assert(2 * NW == N, "bf16 words");
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            f[2 * i] = __uint_as_float(x.w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(x.w[i] & 0xffff0000u);
+        }
+    } else {
+        static_assert(NW == N, "fp32 words");
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = __uint_as_float(x.w[i]);
+    }
+}
+
+// Two floats as one packed word of T pairs (bf16) or two words (fp32).
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    bf16x2 h;
+    h[0] = static_cast<bf16>(a);
+    h[1] = static_cast<bf16>(b);
+    return __builtin_bit_cast(unsigned, h);
+}
+
+// Eight floats -> eight consecutive T in LDS (16-byte aligned).
+__device__ __forceinline__ void st8(bf16 *p, const float (&f)[8]) {
+    *reinterpret_cast<u32x4 *>(p) =
+        u32x4{pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+}
+__device__ __forceinline__ void st8(float *p, const float (&f)[8]) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{f[0], f[1], f[2], f[3]};
+    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
+// Registers holding one chunk's raw inputs for one preparation thread: one
+// token row, two runs of 4 channels of k, q and log_alpha; 16 bytes of the V
+// slice; one beta.
+template <typename T, int D, int DVS>
+struct ChunkRegs {
+    typedef Cfg<T, D, DVS> G;
+    Raw<G::RW> k[2], q[2];
+    Raw<4> g[2];
+    Raw<4> v;
+    float beta;
+};
+
+// Byte offsets (relative to a chunk's first token) of a preparation
+// thread's loads; loop-invariant, so each chunk only rebuilds the scalar
+// descriptors.
 template <typename T, int D, int DVS>
 struct ChunkOffsets {
     typedef Cfg<T, D, DVS> G;
-    int kq[G::RPT], g[G::RPT], v, b;
-    __device__ ChunkOffsets(int tid, int h, int H, int v0) {
-        const int lane = tid & 63, wave = tid >> 6;
-        const int I = wave >> 1, cb = (wave & 1) * (D / 2);
-        const int rg = lane % G::RGB, cg = lane / G::RGB;
-        const int c0 = cb + 8 * cg;
+    int kq[2], g[2], v, b;
+    __device__ ChunkOffsets(int tid, int row, const int (&c)[2], int h, int H, int v0) {
 #pragma unroll
-        for (int j = 0; j < G::RPT; ++j) {
-            const int r = kBS * I + G::RPT * rg + j;
-            kq[j] = ((r * H + h) * D + c0) * (int)sizeof(T);
-            g[j] = ((r * H + h) * D + c0) * 4;
+        for (int j = 0; j < 2; ++j) {
+            kq[j] = ((row * H + h) * D + c[j]) * (int)sizeof(T);
+            g[j] = ((row * H + h) * D + c[j]) * 4;
         }
-        const int vr = tid / (DVS / 8), vc = 8 * (tid % (DVS / 8));
+        const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
         v = ((vr * H + h) * D + v0 + vc) * (int)sizeof(T);
         b = (tid * H + h) * 4;
     }
 };
 
-// The next chunk's registers are loaded in three parts, issued in different
-// phases so the vector memory unit drains them in the background.
 template <typename T, int D, int DVS>
-__device__ __forceinline__ void load_kq(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
-                                        const ChunkOffsets<T, D, DVS> &o) {
+__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
+                                           const ChunkOffsets<T, D, DVS> &o, int tid) {
+    typedef Cfg<T, D, DVS> G;
 #pragma unroll
-    for (int j = 0; j < Cfg<T, D, DVS>::RPT; ++j) {
-        R.k[j] = buf8<T>(s.k, o.kq[j]);
-        R.q[j] = buf8<T>(s.q, o.kq[j]);
+    for (int j = 0; j < 2; ++j) {
+        R.k[j] = buf_load<G::RW>(s.k, o.kq[j]);
+        R.q[j] = buf_load<G::RW>(s.q, o.kq[j]);
+        R.g[j] = buf_load<4>(s.g, o.g[j]);
     }
+    if (tid < G::VTH) R.v = buf_load<4>(s.v, o.v);
+    if (tid < kC) R.beta = __uint_as_float(buf_load<1>(s.b, o.b).w[0]);
 }
-template <typename T, int D, int DVS>
-__device__ __forceinline__ void load_g(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
-                                       const ChunkOffsets<T, D, DVS> &o) {
+
+// DPP helpers (all lanes active).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf,
+                                                      false));
+}
+// every lane of a group of 4 receives x from lane SRC of its group
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float x) { return dpp<SRC * 0x55, 0xf>(x); }
+
+// ------------------------------------------------------------ scan products
+// A-operand fragment of contraction block kb for the 16 rows starting at
+// `row0` (leading dimension ld, physical order), and the MFMA with a B operand
+// taken from accumulator tiles (bf16: two stacked 16x16 tiles; fp32: one).
+template <typename T> struct ScanMma;
+template <> struct ScanMma<bf16> {
+    typedef bf16x8 Frag;
+    __device__ static Frag a(const bf16 *row0, int ld, int kb, int lane) {
+        return *reinterpret_cast<const bf16x8 *>(row0 + (lane & 15) * ld + 32 * kb +
+                                                 8 * (lane >> 4));
+    }
+    __device__ static Frag b(const f32x4 &lo, const f32x4 &hi) {
+        Frag f;
 #pragma unroll
-    for (int j = 0; j < Cfg<T, D, DVS>::RPT; ++j) {
-        R.g[j][0] = buf4f(s.g, o.g[j]);
-        R.g[j][1] = buf4f(s.g, o.g[j] + 16);
+        for (int e = 0; e < 4; ++e) {
+            f[e] = static_cast<bf16>(lo[e]);
+            f[4 + e] = static_cast<bf16>(hi[e]);
+        }
+        return f;
     }
+    __device__ static f32x4 mma(f32x4 acc, const Frag &a, const Frag &b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+template <> struct ScanMma<float> {
+    typedef f32x4 Frag;
+    __device__ static Frag a(const float *row0, int ld, int kb, int lane) {
+        return *reinterpret_cast<const f32x4 *>(row0 + (lane & 15) * ld + 16 * kb +
+                                                4 * (lane >> 4));
+    }
+    __device__ static Frag b(const f32x4 &t, const f32x4 &) { return t; }
+    __device__ static f32x4 mma(f32x4 acc, const Frag &a, const Frag &b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// acc += A B for 16x16 blocks over a contraction of 16: A row-major in LDS
+// (leading dimension ld, lane reads 4 consecutive k), B an accumulator tile
+// (its rows are the contraction index).
+template <typename T>
+__device__ __forceinline__ f32x4 mm16(f32x4 acc, const T *A, int ld, const f32x4 &B, int lane);
+template <>
+__device__ __forceinline__ f32x4 mm16<bf16>(f32x4 acc, const bf16 *A, int ld, const f32x4 &B,
+                                            int lane) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(A + (lane & 15) * ld + 4 * (lane >> 4));
+    bf16x4 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = static_cast<bf16>(B[e]);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                      __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
 }
-template <typename T, int D, int DVS>
-__device__ __forceinline__ void load_vb(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
-                                        const ChunkOffsets<T, D, DVS> &o, int tid) {
-    R.v = tid < Cfg<T, D, DVS>::VTH ? buf8<T>(s.v, o.v) : Vec8<T>::zero();
-    R.beta = tid < kC ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s.b, o.b, 0, 0)) : 0.f;
+template <>
+__device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, const f32x4 &B,
+                                             int lane) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(A + (lane & 15) * ld + 4 * (lane >> 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], B[e], acc, 0, 0, 0);
+    return acc;
 }
 
 template <typename T, int D, int DVS>
-__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
+__global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
@@ -237,30 +334,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int total_tokens, int H, int units, int units_per_xcd) {
     typedef Cfg<T, D, DVS> G;
     typedef Mma<T> M;
-    constexpr int KS = M::KSTEP;
+    typedef ScanMma<T> SM;
     constexpr int NS = D / DVS;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[G::BYTES];
-    T *sKP = reinterpret_cast<T *>(smem + G::oKP);
-    T *sQP = reinterpret_cast<T *>(smem + G::oQP);
-    T *sKM = reinterpret_cast<T *>(smem + G::oKM);
-    T *sX = reinterpret_cast<T *>(smem + G::oX);
-    float *sScr = reinterpret_cast<float *>(smem + G::oScr);
-    T *sO = reinterpret_cast<T *>(smem + G::oO);
-    float *sA = reinterpret_cast<float *>(smem + G::oA);
-    T *sDL = reinterpret_cast<T *>(smem + G::oDL);
-    float *sAt = reinterpret_cast<float *>(smem + G::oAt);
-    T *sKendT = reinterpret_cast<T *>(smem + G::oKendT);
-    T *sMqk = reinterpret_cast<T *>(smem + G::oMqk);
-    T *sTr = reinterpret_cast<T *>(smem + G::oTr);
-    T *sTt = reinterpret_cast<T *>(smem + G::oTt);
-    T *sTd = reinterpret_cast<T *>(smem + G::oTd);
-    T *sS = reinterpret_cast<T *>(smem + G::oS);
-    T *sV = reinterpret_cast<T *>(smem + G::oV);
-    float *sBeta = reinterpret_cast<float *>(smem + G::oBeta);
-    float *sTot = reinterpret_cast<float *>(smem + G::oTot);
-    float *sGam = reinterpret_cast<float *>(smem + G::oGam);
-    int *sFlag = reinterpret_cast<int *>(smem + G::oFlag);
 
     // XCD-aware unit order: workgroups are dealt to the 8 XCDs round-robin,
     // so give each XCD a contiguous run of units; the NS slices of one
@@ -286,492 +363,365 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
     const int nchunks = (int)((tend - tbeg + kC - 1) / kC);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: the role branches below contain barriers and
+    // must be uniform branches, never exec-masked ones
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, l4 = lane >> 4;
 
-    // Upper off-diagonal blocks of Mqk and T' are never written: zero once.
-    for (int i = tid; i < kC * kC; i += kThreads) {
-        const int r = i / kC, c = i % kC;
-        if (c / kBS > r / kBS) {
-            sMqk[r * G::LDC + c] = from_f32<T>(0.f);
-            sTr[r * G::LDC + c] = from_f32<T>(0.f);
+    // The upper-right 16x16 block of Mqk is never written: zero it once in
+    // both buffer sets.
+    for (int i = tid; i < 2 * kBS * kBS; i += G::THREADS) {
+        unsigned char *set = smem + (i / (kBS * kBS)) * G::SET;
+        const int r = (i / kBS) % kBS, c = phys<T>(kBS + i % kBS);
+        reinterpret_cast<T *>(set + G::sMQ)[r * G::LDT + c] = from_f32<T>(0.f);
+    }
+
+    // The two wave groups run separate loops with the same number of
+    // workgroup barriers (one before the loop, three per chunk), so each
+    // group keeps only its own loop-carried registers.
+    if (wave < G::PW) {
+        T *sKD = reinterpret_cast<T *>(smem + G::oKD);
+        T *sQD = reinterpret_cast<T *>(smem + G::oQD);
+        T *sKM = reinterpret_cast<T *>(smem + G::oKM);
+        float *sAt = reinterpret_cast<float *>(smem + G::oAt);
+        // thread map: token row r = lane % 32, physical channel block pb (8
+        // entries) = 2 wave + lane / 32, i.e. two runs of 4 logical channels
+        const int r = lane & 31;
+        const int pb = 2 * wave + (lane >> 5);
+        int crun[2];
+        if constexpr (sizeof(T) == 2) {
+            crun[0] = 32 * (pb >> 2) + 4 * (pb & 3);
+            crun[1] = crun[0] + 16;
+        } else {
+            crun[0] = 8 * pb;
+            crun[1] = crun[0] + 4;
         }
-    }
+        const bool blk1 = r >= kBS;  // rows of block 1
+        const ChunkOffsets<T, D, DVS> offs(tid, r, crun, h, H, v0);
+        ChunkRegs<T, D, DVS> R;
+        if (nchunks > 0)
+            load_chunk(R, chunk_src(q, k, v, log_alpha, beta, tbeg,
+                                    (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D),
+                       offs, tid);
+        __syncthreads();
 
-    // fp32 master state: wave w owns state rows (key channels) 16w..16w+15
-    // for all DVS value columns, in MFMA accumulator layout.
-    const bool owns_state = wave < G::NRT;
-    const int64_t sbase = ((int64_t)n * H + h) * D * D;  // M = S^T: [d_v][d_k]
-    f32x4 Sm[G::NCT];
+        for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
+            const bool on = tick < nchunks;  // prepares chunk `tick`
+            unsigned char *PS = smem + (tick & 1) * G::SET;
+            T *pKP = reinterpret_cast<T *>(PS + G::sKP);
+            T *pQP = reinterpret_cast<T *>(PS + G::sQP);
+            T *pKET = reinterpret_cast<T *>(PS + G::sKET);
+            T *pMQ = reinterpret_cast<T *>(PS + G::sMQ);
+            T *pT3 = reinterpret_cast<T *>(PS + G::sT3);
+            T *pV = reinterpret_cast<T *>(PS + G::sV);
+            float *pGam = reinterpret_cast<float *>(PS + G::sGam);
+            float *pF1 = reinterpret_cast<float *>(PS + G::sF1);
+            float *pBeta = reinterpret_cast<float *>(PS + G::sBeta);
+
+            // ------------------------------------------------------ phase 1
+            if (on) {
+                float kf[8], qf[8], d[8];
 #pragma unroll
-    for (int ct = 0; ct < G::NCT; ++ct) {
-        Sm[ct] = zero4();
-        if (owns_state && initial_state)
-            Sm[ct] = *reinterpret_cast<const f32x4 *>(
-                initial_state + sbase + (int64_t)(v0 + 16 * ct + l16) * D + 16 * wave + 4 * l4);
-        if (owns_state)
-            store4(sS + (16 * ct + l16) * G::LDK + 16 * wave + 4 * l4, Sm[ct][0], Sm[ct][1],
-                   Sm[ct][2], Sm[ct][3]);
-    }
-
-    // prep thread map: block I = wave / 2, channels c0..c0+7, rows r_j.
-    const int pI = wave >> 1;
-    const int prg = lane % G::RGB, pcg = lane / G::RGB;
-    const int pc0 = (wave & 1) * (D / 2) + 8 * pcg;
-
-    const ChunkOffsets<T, D, DVS> offs(tid, h, H, v0);
-    ChunkRegs<T, D, DVS> R;
-    if (nchunks > 0) {
-        const ChunkSrc s0 = chunk_src(q, k, v, log_alpha, beta, tbeg,
-                                      (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D);
-        load_kq(R, s0, offs);
-        load_g(R, s0, offs);
-        load_vb(R, s0, offs, tid);
-    }
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int64_t tok0 = tbeg + (int64_t)ch * kC;
-        const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
-        const int64_t ntok0 = tok0 + kC;
-        const int nnext = ch + 1 < nchunks ? (int)((tend - ntok0) < kC ? (tend - ntok0) : kC) : 0;
-        const ChunkSrc nsrc = chunk_src(q, k, v, log_alpha, beta, ntok0, nnext, H, D);
-
-        int npass = 1;  // 4 when the chunk is redone as 16-token windows
-        for (int pass = 0; pass < npass; ++pass) {
-            // A windowed pass keeps the rows of one 16-token block; the rows of
-            // a thread all lie in block pI, so masking is per thread.
-            const int lo = npass == 1 ? 0 : kBS * pass;
-            const int hi = npass == 1 ? kC : lo + kBS;
-            const bool keep = npass == 1 || pI == pass;
-
-            // -------------------------------------------------------- prep
-            float P[G::RPT][8];
-            {
-                float gl[G::RPT][8];
+                for (int j = 0; j < 2; ++j) {
+                    unpack<T, 4>(R.k[j], kf + 4 * j);
+                    unpack<T, 4>(R.q[j], qf + 4 * j);
+                    unpack<float, 4>(R.g[j], d + 4 * j);
+                }
+                // block-relative inclusive prefix of the log2-gates: the 16
+                // lanes of a DPP row are the 16 tokens of one block
+                float erho[8];
 #pragma unroll
-                for (int j = 0; j < G::RPT; ++j) {
+                for (int i = 0; i < 8; ++i) {
+                    float x = d[i] * kLog2e;
+                    x += dpp_row_shr<1>(x);
+                    x += dpp_row_shr<2>(x);
+                    x += dpp_row_shr<4>(x);
+                    x += dpp_row_shr<8>(x);
+                    d[i] = x;
+                    // rho = Gamma_15 (block 0's total): lane 15 of this row for
+                    // block 0, of the previous row for block 1
+                    const float own = dpp<0x15f, 0xf>(x);   // row_newbcast:15
+                    const float prev = dpp<0x142, 0xa>(x);  // row_bcast:15
+                    erho[i] = fast_exp2(blk1 ? prev : own);
+                }
+                float kt[8], ep[8];
+                {
+                    float kp[8], qp[8], km[8], kd[8], qd[8];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        gl[j][e] = keep ? R.g[j][0][e] * kLog2e : 0.f;
-                        gl[j][4 + e] = keep ? R.g[j][1][e] * kLog2e : 0.f;
+                    for (int i = 0; i < 8; ++i) {
+                        ep[i] = fast_exp2(d[i]);
+                        const float em = fast_exp2(-d[i]);
+                        kd[i] = kf[i] * ep[i];  // block-relative (= chunk-relative in block 0)
+                        qd[i] = qf[i] * ep[i];
+                        const float sc = blk1 ? erho[i] : 1.f;
+                        kp[i] = kd[i] * sc;  // chunk-relative
+                        qp[i] = qd[i] * sc;
+                        km[i] = kf[i] * em;
+                        kt[i] = km[i] * (blk1 ? 1.f : erho[i]);  // K e^{rho - Gamma}
+                    }
+                    st8(pKP + r * G::LDK + 8 * pb, kp);
+                    st8(pQP + r * G::LDK + 8 * pb, qp);
+                    st8(sKM + r * G::LDK + 8 * pb, km);
+                    if (blk1) {
+                        st8(sKD + (r - kBS) * G::LDK + 8 * pb, kd);
+                        st8(sQD + (r - kBS) * G::LDK + 8 * pb, qd);
                     }
                 }
-                // inclusive prefix over this thread's rows, then over the lanes
-                // of the 16-row block (consecutive lanes of one DPP row).
-                float btot[8];
+                if (r == kC - 1) {
+                    // f1 = e^{Gamma_last - rho}, gamma = e^{Gamma_last}, two runs of 4
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float run = 0.f;
-#pragma unroll
-                    for (int j = 0; j < G::RPT; ++j) {
-                        run += gl[j][e];
-                        P[j][e] = run;
+                    for (int j = 0; j < 2; ++j) {
+                        *reinterpret_cast<f32x4 *>(pF1 + crun[j]) =
+                            f32x4{ep[4 * j], ep[4 * j + 1], ep[4 * j + 2], ep[4 * j + 3]};
+                        *reinterpret_cast<f32x4 *>(pGam + crun[j]) =
+                            f32x4{erho[4 * j] * ep[4 * j], erho[4 * j + 1] * ep[4 * j + 1],
+                                  erho[4 * j + 2] * ep[4 * j + 2], erho[4 * j + 3] * ep[4 * j + 3]};
                     }
-                    float x = run;
-                    float y = dpp_row_shr<1>(x);
-                    if (prg >= 1) x += y;
-                    y = dpp_row_shr<2>(x);
-                    if (prg >= 2) x += y;
-                    y = dpp_row_shr<4>(x);
-                    if (prg >= 4) x += y;
-                    if (G::RGB == 16) {
-                        y = dpp_row_shr<8>(x);
-                        if (prg >= 8) x += y;
-                    }
-                    const float excl = x - run;
+                }
+                // (K e^{rho - Gamma})^T, channel rows, token pairs: the even
+                // lane of a pair stores run 0 (channels 0-3), the odd lane run 1
+                {
+                    const bool odd = r & 1;
+                    T *dst = pKET + crun[odd ? 1 : 0] * G::LDT + phys<T>(r & ~1);
 #pragma unroll
-                    for (int j = 0; j < G::RPT; ++j) P[j][e] += excl;
-                    btot[e] = __shfl(x, lane | (G::RGB - 1), 64);
+                    for (int j = 0; j < 4; ++j) {
+                        const float own = odd ? kt[4 + j] : kt[j];
+                        const float send = odd ? kt[j] : kt[4 + j];
+                        const float recv = dpp<0xb1, 0xf>(send);  // quad_perm [1,0,3,2]
+                        const float lo = odd ? recv : own, hi = odd ? own : recv;
+                        if constexpr (sizeof(T) == 2)
+                            *reinterpret_cast<unsigned *>(dst + j * G::LDT) = pack2(lo, hi);
+                        else
+                            *reinterpret_cast<f32x2 *>(dst + j * G::LDT) = f32x2{lo, hi};
+                    }
                 }
-                if (prg == G::RGB - 1) {
-                    store4(sTot + pI * D + pc0, btot[0], btot[1], btot[2], btot[3]);
-                    store4(sTot + pI * D + pc0 + 4, btot[4], btot[5], btot[6], btot[7]);
+                if (tid < G::VTH) {
+                    const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
+                    *reinterpret_cast<u32x4 *>(pV + vr * G::LDV + vc) =
+                        u32x4{R.v.w[0], R.v.w[1], R.v.w[2], R.v.w[3]};
                 }
+                if (tid < kC) pBeta[tid] = R.beta;
+                // the registers are free: start loading the next chunk
+                const int64_t ntok0 = tbeg + (int64_t)(tick + 1) * kC;
+                if (tick + 1 < nchunks)
+                    load_chunk(R, chunk_src(q, k, v, log_alpha, beta, ntok0,
+                                            (int)((tend - ntok0) < kC ? (tend - ntok0) : kC), H,
+                                            D),
+                               offs, tid);
             }
-            float vf[8];
-            Vec8<T>::to_float(R.v, vf);
-            {
-                const int vr = tid / (DVS / 8);
-                if (vr < lo || vr >= hi) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) vf[e] = 0.f;
-                }
-            }
-            const float beta_r = (tid >= lo && tid < hi) ? R.beta : 0.f;
             __syncthreads();
 
-            {
-                float Gb[8], Gend[8];
+            // ------------------------------------------------------ phase 2
+            // tiles 0-5 = A_00 (then T_00), A_11 (then T_11), A_10, Mqk_00,
+            // Mqk_11, Mqk_10; wave w takes tiles w and w + PW (products over
+            // physical channels, both operands in the same order)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Gb[e] = 0.f;
-                    Gend[e] = 0.f;
-                }
-#pragma unroll
-                for (int J = 0; J < kNB; ++J) {
-                    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(sTot + J * D + pc0);
-                    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(sTot + J * D + pc0 + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (J < pI) {
-                            Gb[e] += t0[e];
-                            Gb[4 + e] += t1[e];
-                        }
-                        Gend[e] += t0[e];
-                        Gend[4 + e] += t1[e];
-                    }
-                }
-                float fend[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fend[e] = fast_exp2(Gend[e]);
-                float mx = 0.f;
-                float ke[G::RPT][8];
-#pragma unroll
-                for (int j = 0; j < G::RPT; ++j) {
-                    float kf[8], qf[8], kp[8], qp[8], km[8];
-                    Vec8<T>::to_float(R.k[j], kf);
-                    Vec8<T>::to_float(R.q[j], qf);
-                    if (!keep) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            kf[e] = 0.f;
-                            qf[e] = 0.f;
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float gam = Gb[e] + P[j][e];
-                        mx = fmaxf(mx, fabsf(gam));
-                        const float ep = fast_exp2(gam);
-                        const float em = fast_exp2(-gam);
-                        kp[e] = kf[e] * ep;
-                        qp[e] = qf[e] * ep;
-                        km[e] = kf[e] * em;
-                        ke[j][e] = km[e] * fend[e];
-                    }
-                    const int r = kBS * pI + G::RPT * prg + j;
-                    store8(sKP + r * G::LDK + pc0, kp);
-                    store8(sQP + r * G::LDK + pc0, qp);
-                    store8(sKM + r * G::LDK + pc0, km);
-                }
-                // NaN compares false: a non-finite gate also takes the windowed path
-                const bool bad = !(mx < kMaxLog2Decay);
-                const unsigned long long any = __ballot(bad);
-                if (lane == 0) sFlag[wave] = any != 0ull;
-                // K_end^T: key-channel rows, token columns (RPT consecutive tokens)
-                const int r0 = kBS * pI + G::RPT * prg;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    if constexpr (G::RPT == 2) {
-                        store2(sKendT + (pc0 + e) * G::LDC + kend_col(pc0 + e, r0), ke[0][e],
-                               ke[1][e]);
-                    } else {
-                        sKendT[(pc0 + e) * G::LDC + kend_col(pc0 + e, r0)] =
-                            from_f32<T>(ke[0][e]);
-                    }
-                }
-                if (tid < D) {
-                    // gamma = e^{Gamma_last} for key channel tid
-                    float s = 0.f;
-#pragma unroll
-                    for (int J = 0; J < kNB; ++J) s += sTot[J * D + tid];
-                    sGam[tid] = fast_exp2(s);
-                }
-            }
-            if (tid < G::VTH) {
-                const int vr = tid / (DVS / 8), vc = 8 * (tid % (DVS / 8));
-                store8(sV + vr * G::LDV + vc, vf);
-            }
-            if (tid < kC) sBeta[tid] = beta_r;
-            __syncthreads();
-
-            {
-                bool unsafe = false;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) unsafe |= sFlag[w] != 0;
-                if (npass == 1 && unsafe) {
-                    npass = kNB;  // redo this chunk as four 16-token windows
-                    pass = -1;
-                    continue;
-                }
-            }
-            // Prefetch the next chunk's inputs once this chunk's last pass has
-            // consumed the registers; they arrive while the chunk is computed.
-            const bool prefetch = pass == npass - 1 && nnext > 0;
-            if (prefetch) load_kq(R, nsrc, offs);
-
-            // -------------------------------------------------------- A, Mqk
-#pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                const int t = wave + kWaves * s;
-                if (t >= 20) continue;
-                const bool isA = t < 10;
-                int I, J;
-                tile_ij(isA ? t : t - 10, I, J);
-                const T *left = (isA ? sKP : sQP) + kBS * I * G::LDK;
-                const T *right = sKM + kBS * J * G::LDK;
-                f32x4 acc = tile_mma<T, D>(zero4(), left, G::LDK, right, G::LDK, lane);
-                if (isA) {
+            for (int u = 0; u < 2; ++u) {
+                const int tile = wave + u * G::PW;
+                if (!on || tile >= 6) continue;
+                const bool isA = tile < 3;
+                const int t = isA ? tile : tile - 3;  // 0: (0,0), 1: (1,1), 2: (1,0)
+                const int I = t == 0 ? 0 : 1, J = t == 1 ? 1 : 0;
+                const T *left = t == 0 ? (isA ? pKP : pQP)
+                                       : (t == 1 ? (isA ? sKD : sQD)
+                                                 : (isA ? pKP : pQP) + kBS * G::LDK);
+                const f32x4 acc = tile_mma<T, D>(zero4(), left, G::LDK, sKM + kBS * J * G::LDK,
+                                                 G::LDK, lane);
+                if (!isA) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * l4 + e;
-                        float val = acc[e] * sBeta[kBS * I + r];
-                        if (I == J && l16 >= r) val = 0.f;
-                        acc[e] = val;
-                        sA[(kBS * I + r) * G::LDA + kBS * J + l16] = val;
+                        const int rr = 4 * l4 + e;
+                        const float val = (I == J && l16 > rr) ? 0.f : acc[e];
+                        pMQ[(kBS * I + rr) * G::LDT + phys<T>(kBS * J + l16)] = from_f32<T>(val);
                     }
-                    if (I == J)  // transposed copy of the diagonal block
-                        store4(sAt + (I * kBS + l16) * G::LDAT + 4 * l4, acc[0], acc[1], acc[2],
-                               acc[3]);
+                } else if (I != J) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = 4 * l4 + e;  // A_10 = diag(b_1) (K+ K-^T)_10
+                        pT3[G::B_T16 / G::SZ + rr * G::LDTT + l16] =
+                            from_f32<T>(acc[e] * pBeta[kBS + rr]);
+                    }
                 } else {
+                    // diagonal block: strictly lower part, stored transposed
+                    // (row c of At = column c of A_II), then inverted here
+                    float a[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * l4 + e;
-                        const float val = (I == J && l16 > r) ? 0.f : acc[e];
-                        sMqk[(kBS * I + r) * G::LDC + kBS * J + l16] = from_f32<T>(val);
+                        const int rr = 4 * l4 + e;
+                        a[e] = l16 < rr ? acc[e] * pBeta[kBS * I + rr] : 0.f;
                     }
-                }
-            }
-            __syncthreads();
-
-            if (prefetch) load_g(R, nsrc, offs);
-
-            // ------------------------------------- T diagonal || [K+; Q+] S
-            f32x4 PQ[G::NCT];
+                    float *At = sAt + I * kBS * G::LDAT;
+                    store4(At + l16 * G::LDAT + 4 * l4, a[0], a[1], a[2], a[3]);
+                    wave_lds_fence();
+                    // lane 4 j + g holds rows 4 g .. 4 g + 3 of column j of
+                    // (I + A_II)^{-1}; forward substitution, one column of A per
+                    // step, the pivot broadcast inside the lane quad
+                    const int j = lane >> 2, g = lane & 3;
+                    float s[4];
 #pragma unroll
-            for (int ct = 0; ct < G::NCT; ++ct) PQ[ct] = zero4();
-            if (wave == 0) {
-                // lane 16*I + j: column j of (I + A_II)^{-1}, right-looking
-                const int I = l4, j = l16;
-                const float *At = sAt + I * kBS * G::LDAT;
-                float s[kBS];
+                    for (int e = 0; e < 4; ++e) s[e] = (4 * g + e == j) ? 1.f : 0.f;
+                    constexpr int LA = 4;  // columns of A read ahead of their step
+                    f32x4 col[kBS - 1];
 #pragma unroll
-                for (int r = 0; r < kBS; ++r) s[r] = (r == j) ? 1.f : 0.f;
-                // column i of A_II (all 16 lanes of a group read the same row
-                // of the transposed block: an LDS broadcast); one column of
-                // lookahead, no more, to bound register use.
-                f32x4 cur[kBS / 4], nxt[kBS / 4];
+                    for (int i = 0; i < LA; ++i)
+                        col[i] = *reinterpret_cast<const f32x4 *>(At + i * G::LDAT + 4 * g);
 #pragma unroll
-                for (int c4 = 0; c4 < kBS / 4; ++c4)
-                    cur[c4] = *reinterpret_cast<const f32x4 *>(At + 4 * c4);
-#pragma unroll
-                for (int i = 0; i < kBS - 1; ++i) {
-                    if (i + 1 < kBS - 1) {
-#pragma unroll
-                        for (int c4 = 0; c4 < kBS / 4; ++c4)
-                            nxt[c4] = *reinterpret_cast<const f32x4 *>(At + (i + 1) * G::LDAT +
-                                                                       4 * c4);
-                    }
-                    const float xi = s[i];
-#pragma unroll
-                    for (int r = i + 1; r < kBS; ++r) s[r] -= cur[r >> 2][r & 3] * xi;
-#pragma unroll
-                    for (int c4 = 0; c4 < kBS / 4; ++c4) cur[c4] = nxt[c4];
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const float bj = sBeta[kBS * I + j];
-#pragma unroll
-                for (int r = 0; r < kBS; ++r) {
-                    sTd[I * G::TDB + r * G::LDD + j] = from_f32<T>(s[r]);
-                    sTr[(kBS * I + r) * G::LDC + kBS * I + j] = from_f32<T>(s[r] * bj);
-                }
-#pragma unroll
-                for (int r = 0; r < kBS; r += 4)
-                    store4(sTt + (kBS * I + j) * G::LDC + kBS * I + r, s[r], s[r + 1], s[r + 2],
-                           s[r + 3]);
-            } else if (wave >= 4) {
-                // rows 16i..16i+15 of K+ S (-> X = V - K+ S) and of Q+ S
-                const int i = wave - 4;
-                f32x4 PK[G::NCT];
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct) PK[ct] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < D; kk += KS) {
-                    const typename M::Frag ak = M::load(sKP + kBS * i * G::LDK + kk, G::LDK, lane);
-                    const typename M::Frag aq = M::load(sQP + kBS * i * G::LDK + kk, G::LDK, lane);
-#pragma unroll
-                    for (int ct = 0; ct < G::NCT; ++ct) {
-                        const typename M::Frag b =
-                            M::load(sS + 16 * ct * G::LDK + kk, G::LDK, lane);
-                        PK[ct] = M::mma(ak, b, PK[ct]);
-                        PQ[ct] = M::mma(aq, b, PQ[ct]);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct) {
-                    float x[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = kBS * i + 4 * l4 + e;
-                        x[e] = to_f32(sV[r * G::LDV + 16 * ct + l16]) - PK[ct][e];
-                    }
-                    store4(sX + (16 * ct + l16) * G::LDC + kBS * i + 4 * l4, x[0], x[1], x[2],
-                           x[3]);
-                }
-            }
-            __syncthreads();
-
-            if (prefetch) load_vb(R, nsrc, offs, tid);
-
-            // Off-diagonal blocks: T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ, level by level.
-#pragma unroll
-            for (int lvl = 1; lvl < kNB; ++lvl) {
-                if (wave < kNB - lvl) {
-                    const int J = wave, I = wave + lvl;
-                    f32x4 acc = zero4();
-                    f32x4 Y = zero4();
-                    if constexpr (sizeof(T) == 2) {
-                        for (int K = J; K < I; ++K) {
-                            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(
-                                sA + (kBS * I + l16) * G::LDA + kBS * K + 4 * l4);
-                            bf16x4 ab;
-                            ab[0] = static_cast<bf16>(a4[0]);
-                            ab[1] = static_cast<bf16>(a4[1]);
-                            ab[2] = static_cast<bf16>(a4[2]);
-                            ab[3] = static_cast<bf16>(a4[3]);
-                            const bf16x4 bb = *reinterpret_cast<const bf16x4 *>(
-                                sTt + (kBS * J + l16) * G::LDC + kBS * K + 4 * l4);
-                            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                                __builtin_bit_cast(i16x4, ab), __builtin_bit_cast(i16x4, bb), acc,
-                                0, 0, 0);
+                    for (int i = 0; i < kBS - 1; ++i) {
+                        if (i + LA < kBS - 1)
+                            col[i + LA] = *reinterpret_cast<const f32x4 *>(
+                                At + (i + LA) * G::LDAT + 4 * g);
+                        float x;
+                        switch (i >> 2) {  // pivot T[i][j] from quad lane i / 4
+                            case 0: x = quad_bcast<0>(s[i & 3]); break;
+                            case 1: x = quad_bcast<1>(s[i & 3]); break;
+                            case 2: x = quad_bcast<2>(s[i & 3]); break;
+                            default: x = quad_bcast<3>(s[i & 3]); break;
                         }
-                        const bf16x4 ta = *reinterpret_cast<const bf16x4 *>(
-                            sTd + I * G::TDB + l16 * G::LDD + 4 * l4);
-                        bf16x4 xb;
-                        xb[0] = static_cast<bf16>(-acc[0]);
-                        xb[1] = static_cast<bf16>(-acc[1]);
-                        xb[2] = static_cast<bf16>(-acc[2]);
-                        xb[3] = static_cast<bf16>(-acc[3]);
-                        Y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                            __builtin_bit_cast(i16x4, ta), __builtin_bit_cast(i16x4, xb), Y, 0, 0,
-                            0);
-                    } else {
-                        for (int K = J; K < I; ++K) {
+                        // A[rr][i] = 0 for rr <= i, so settled rows are unchanged
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) {
-                                const float a =
-                                    sA[(kBS * I + l16) * G::LDA + kBS * K + 4 * s + l4];
-                                const float b = to_f32(
-                                    sTt[(kBS * J + l16) * G::LDC + kBS * K + 4 * s + l4]);
-                                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-                            }
-                        }
-                        float *scr = sScr + wave * kBS * G::LDX;
-                        store4(scr + l16 * G::LDX + 4 * l4, -acc[0], -acc[1], -acc[2], -acc[3]);
-                        wave_lds_fence();
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const float a = to_f32(sTd[I * G::TDB + l16 * G::LDD + 4 * s + l4]);
-                            const float b = scr[l16 * G::LDX + 4 * s + l4];
-                            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, Y, 0, 0, 0);
-                        }
+                        for (int e = 0; e < 4; ++e) s[e] -= col[i][e] * x;
                     }
-                    // lane holds T_IJ[4*l4 + e][l16]
-                    store4(sTt + (kBS * J + l16) * G::LDC + kBS * I + 4 * l4, Y[0], Y[1], Y[2],
-                           Y[3]);
-                    const float bj = sBeta[kBS * J + l16];
+                    // T'_00 = T_00 diag(b_0) (block 0 of T3) or T_11 (block 2)
+                    const float bj = I == 0 ? pBeta[j] : 1.f;
+                    T *dstT = pT3 + (2 * I) * (G::B_T16 / G::SZ);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        sTr[(kBS * I + 4 * l4 + e) * G::LDC + kBS * J + l16] =
-                            from_f32<T>(Y[e] * bj);
+                        dstT[(4 * g + e) * G::LDTT + j] = from_f32<T>(s[e] * bj);
                 }
-                __syncthreads();
-            }
-
-            // ------------------------------------------------------- scan
-            // Delta = T' X (waves 0-3, lower-triangular k range), stored transposed.
-            if (wave < 4) {
-                const int rt = wave;
-                const int nks = (kBS * (rt + 1) + KS - 1) / KS;
-                f32x4 acc[G::NCT];
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct) acc[ct] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < kC / KS; ++ks) {
-                    if (ks < nks) {
-                        const typename M::Frag a =
-                            M::load(sTr + kBS * rt * G::LDC + ks * KS, G::LDC, lane);
-#pragma unroll
-                        for (int ct = 0; ct < G::NCT; ++ct)
-                            acc[ct] = M::mma(
-                                a, M::load(sX + 16 * ct * G::LDC + ks * KS, G::LDC, lane),
-                                acc[ct]);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct)
-                    store4(sDL + (16 * ct + l16) * G::LDC + kBS * rt + 4 * l4, acc[ct][0],
-                           acc[ct][1], acc[ct][2], acc[ct][3]);
             }
             __syncthreads();
 
-            // O = Q+ S + Mqk Delta (waves 4-7), staged for a coalesced store.
-            if (wave >= 4) {
-                const int rt = wave - 4;
-                const int nks = (kBS * (rt + 1) + KS - 1) / KS;
-#pragma unroll
-                for (int ks = 0; ks < kC / KS; ++ks) {
-                    if (ks < nks) {
-                        const typename M::Frag a =
-                            M::load(sMqk + kBS * rt * G::LDC + ks * KS, G::LDC, lane);
-#pragma unroll
-                        for (int ct = 0; ct < G::NCT; ++ct)
-                            PQ[ct] = M::mma(
-                                a, M::load(sDL + 16 * ct * G::LDC + ks * KS, G::LDC, lane),
-                                PQ[ct]);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sO[(kBS * rt + 4 * l4 + e) * G::LDO + 16 * ct + l16] =
-                            from_f32<T>(PQ[ct][e]);
-            }
-            // S <- Diag(gamma) S + Kend^T Delta on the owning waves.
-            if (owns_state) {
-                float gm[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gm[e] = sGam[16 * wave + 4 * l4 + e];
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Sm[ct][e] *= gm[e];
-#pragma unroll
-                for (int kk = 0; kk < kC; kk += KS) {
-                    const int c = 16 * wave + l16;
-                    const int t0 = kk + (KS == 32 ? 8 * l4 : l4);
-                    const typename M::Frag a = *reinterpret_cast<const typename M::Frag *>(
-                        sKendT + c * G::LDC + kend_col(c, t0));
-#pragma unroll
-                    for (int ct = 0; ct < G::NCT; ++ct)
-                        Sm[ct] = M::mma(a, M::load(sDL + 16 * ct * G::LDC + kk, G::LDC, lane),
-                                        Sm[ct]);
-                }
-#pragma unroll
-                for (int ct = 0; ct < G::NCT; ++ct)
-                    store4(sS + (16 * ct + l16) * G::LDK + 16 * wave + 4 * l4, Sm[ct][0],
-                           Sm[ct][1], Sm[ct][2], Sm[ct][3]);
-            }
-            __syncthreads();
-
-            // Output rows of this pass.
-            if (tid < G::VTH) {
-                const int orow = tid / (DVS / 8), ocol = 8 * (tid % (DVS / 8));
-                if (orow >= lo && orow < hi && orow < nvalid) {
-                    float of[8];
-                    Vec8<T>::to_float(load8(sO + orow * G::LDO + ocol), of);
-                    store8(out + ((tok0 + orow) * H + h) * (int64_t)D + v0 + ocol, of);
-                }
-            }
         }
+        return;
     }
 
-    if (final_state && owns_state) {
+    // ------------------------------------------------------------------ scan
+    // wave PW + ct owns value columns v0 + 16 ct .. + 15 of the state for all
+    // d_k rows: NRT fp32 accumulator tiles (lane: value column 16 ct + l16,
+    // key rows 16 t + 4 l4 + e)
+    const int ct = wave - G::PW;
+    T *sO = reinterpret_cast<T *>(smem + G::oO) + ct * kC * G::LDO;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D;  // M = S^T: [d_v][d_k]
+    const int vcol = v0 + 16 * ct + l16;
+    f32x4 Sm[G::NRT];
 #pragma unroll
-        for (int ct = 0; ct < G::NCT; ++ct)
-            *reinterpret_cast<f32x4 *>(final_state + sbase + (int64_t)(v0 + 16 * ct + l16) * D +
-                                       16 * wave + 4 * l4) = Sm[ct];
+    for (int t = 0; t < G::NRT; ++t)
+        Sm[t] = initial_state ? *reinterpret_cast<const f32x4 *>(
+                                    initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * l4)
+                              : zero4();
+    __syncthreads();
+
+    for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
+        const bool on = tick > 0;  // scans chunk `tick - 1`
+        const unsigned char *SS = smem + ((tick & 1) ^ 1) * G::SET;
+        const T *cKP = reinterpret_cast<const T *>(SS + G::sKP);
+        const T *cQP = reinterpret_cast<const T *>(SS + G::sQP);
+        const T *cKET = reinterpret_cast<const T *>(SS + G::sKET);
+        const T *cMQ = reinterpret_cast<const T *>(SS + G::sMQ);
+        const T *cT3 = reinterpret_cast<const T *>(SS + G::sT3);
+        const T *cV = reinterpret_cast<const T *>(SS + G::sV);
+        const float *cBeta = reinterpret_cast<const float *>(SS + G::sBeta);
+        const float *cGam = reinterpret_cast<const float *>(SS + G::sGam);
+        const float *cF1 = reinterpret_cast<const float *>(SS + G::sF1);
+        f32x4 Dl[2];  // Delta row tiles (tokens 0-15, 16-31), kept for phase 2
+
+        // ---------------------------------------------------------- phase 1
+        if (on) {
+            const int64_t tok0 = tbeg + (int64_t)(tick - 1) * kC;
+            const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
+            // the state as B operands, one per contraction block
+            typename SM::Frag Sb[D / G::KB];
+#pragma unroll
+            for (int kb = 0; kb < D / G::KB; ++kb) {
+                if constexpr (sizeof(T) == 2)
+                    Sb[kb] = SM::b(Sm[2 * kb], Sm[2 * kb + 1]);
+                else
+                    Sb[kb] = SM::b(Sm[kb], Sm[kb]);
+            }
+            f32x4 PK[2], PQ[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                PK[rt] = zero4();
+                PQ[rt] = zero4();
+#pragma unroll
+                for (int kb = 0; kb < D / G::KB; ++kb) {
+                    PK[rt] = SM::mma(PK[rt], SM::a(cKP + kBS * rt * G::LDK, G::LDK, kb, lane),
+                                     Sb[kb]);
+                    PQ[rt] = SM::mma(PQ[rt], SM::a(cQP + kBS * rt * G::LDK, G::LDK, kb, lane),
+                                     Sb[kb]);
+                }
+            }
+            // X = V - K+ S (accumulator layout: token rows 16 rt + 4 l4 + e)
+            f32x4 X[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    X[rt][e] = to_f32(cV[(kBS * rt + 4 * l4 + e) * G::LDV + 16 * ct + l16]) -
+                               PK[rt][e];
+            // Delta solves (I + A) Delta = diag(b) X block by block:
+            // Delta_0 = T_00 b_0 X_0, Delta_1 = T_11 (b_1 X_1 - A_10 Delta_0)
+            constexpr int T16 = G::B_T16 / G::SZ;
+            Dl[0] = mm16<T>(zero4(), cT3, G::LDTT, X[0], lane);
+            {
+                const f32x4 ad = mm16<T>(zero4(), cT3 + T16, G::LDTT, Dl[0], lane);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(cBeta + kBS + 4 * l4);
+                f32x4 r1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r1[e] = b1[e] * X[1][e] - ad[e];
+                Dl[1] = mm16<T>(zero4(), cT3 + 2 * T16, G::LDTT, r1, lane);
+            }
+            // O = Q+ S + Mqk Delta (Mqk lower triangular)
+            const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
+            const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 0, lane), Db0);
+                if (sizeof(T) == 4 && rt == 1)
+                    PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 1, lane), Db1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sO[(kBS * rt + 4 * l4 + e) * G::LDO + l16] = from_f32<T>(PQ[rt][e]);
+            }
+            wave_lds_fence();
+            // 32 rows x 16 columns of O, 16-byte pieces
+            constexpr int PPR = 16 * (int)sizeof(T) / 16;  // pieces per row
+#pragma unroll
+            for (int p = lane; p < kC * PPR; p += 64) {
+                const int orow = p / PPR, opc = (p % PPR) * G::VE;
+                if (orow < nvalid)
+                    *reinterpret_cast<u32x4 *>(out + ((tok0 + orow) * H + h) * (int64_t)D + v0 +
+                                               16 * ct + opc) =
+                        *reinterpret_cast<const u32x4 *>(sO + orow * G::LDO + opc);
+            }
+        }
+        __syncthreads();
+
+        // ---------------------------------------------------------- phase 2
+        if (on) {
+            // S <- Diag(gamma) S + Diag(f1) (K e^{rho - Gamma})^T Delta
+            const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
+            const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
+#pragma unroll
+            for (int t = 0; t < G::NRT; ++t) {
+                f32x4 acc = SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Db0);
+                if (sizeof(T) == 4)
+                    acc = SM::mma(acc, SM::a(cKET + 16 * t * G::LDT, G::LDT, 1, lane), Db1);
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(cGam + 16 * t + 4 * l4);
+                const f32x4 f1 = *reinterpret_cast<const f32x4 *>(cF1 + 16 * t + 4 * l4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sm[t][e] = gm[e] * Sm[t][e] + f1[e] * acc[e];
+            }
+        }
+        __syncthreads();
+    }
+
+    if (final_state) {
+#pragma unroll
+        for (int t = 0; t < G::NRT; ++t)
+            *reinterpret_cast<f32x4 *>(final_state + sbase + (int64_t)vcol * D + 16 * t +
+                                       4 * l4) = Sm[t];
     }
 }
 
@@ -784,11 +734,11 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
     if (units64 > (int64_t)1 << 30) return -1;
     const int units = (int)units64;
     const int per_xcd = (units + 7) / 8;
-    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS>), dim3(8 * per_xcd), dim3(kThreads), 0,
-                       stream, static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), log_alpha, beta, initial_state, cu_seqlens,
-                       static_cast<T *>(out), final_state, num_seqs, seq_len, total_tokens, H,
-                       units, per_xcd);
+    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS>), dim3(8 * per_xcd),
+                       dim3(Cfg<T, D, DVS>::THREADS), 0, stream, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
+                       initial_state, cu_seqlens, static_cast<T *>(out), final_state, num_seqs,
+                       seq_len, total_tokens, H, units, per_xcd);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

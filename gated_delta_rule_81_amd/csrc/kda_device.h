@@ -44,6 +44,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Native clang vectors only: HIP's float4/uint4 are union-based classes that
 // the optimiser cannot always keep in registers.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 template <typename T> struct Vec8;

@@ -35,8 +35,9 @@
  *     validated on the host before any HIP call, so errors are reported
  *     without touching the device.  Calls on different streams may run
  *     concurrently if their outputs do not overlap.
- *   - Supported now: d_k == d_v in {64, 128}.  Other valid sizes return
- *     KDA_ERR_UNSUPPORTED.
+ *   - Supported now: d_k == d_v in {64, 128}, and for kda_chunk_fwd
+ *     num_heads * d_k <= 8388607 (64 tokens of one tensor must span less
+ *     than 2^31 bytes).  Other valid sizes return KDA_ERR_UNSUPPORTED.
  *
  * Numerics contract: log_alpha must be finite and, within each run of 16
  * tokens that starts at a multiple of 16 from the sequence start, its sum per

@@ -115,6 +115,12 @@ def test_chunk_unsupported(kw):
     assert call_chunk(**kw) == UNSUP
 
 
+def test_chunk_head_count_bound_for_32bit_offsets():
+    # 64 tokens of log_alpha (H * d fp32 each) must span less than 2^31 bytes
+    assert call_chunk(num_heads=65536, batch=1, seq_len=1) == UNSUP
+    assert call_chunk(num_heads=65535, batch=1, seq_len=1) in (DEVICE, OK)
+
+
 @pytest.mark.parametrize("name", ["q", "k", "v", "log_alpha", "initial_state", "out",
                                   "final_state"])
 def test_chunk_misaligned(name):
