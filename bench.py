@@ -39,7 +39,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
-PREFILL_FLOP_PER_TOKEN_HEAD = 140629  # d=128, C=64, triangular products
+# d=128, chunk 32: 6 d^2 for [K+; Q+] S and Kend^T Delta, plus 24,576 for the
+# lower-triangular intra-chunk products (A, Mqk, Delta, Mqk Delta)
+PREFILL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traffic.json")
 
 
@@ -62,10 +64,16 @@ def decode_bytes(B, H, d, esz=2):
 
 
 def source_digest():
+    """sha256 of the prefill kernel's source with comments and blank lines
+    removed, so that comment edits keep the counter summary valid."""
+    import re
     h = hashlib.sha256()
     for name in ("kda_chunk.hip", "kda_device.h"):
-        with open(os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()
 
 
@@ -212,7 +220,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "kda_chunk_fwd B=1 H=96 T=32768 d_k=d_v=128 bf16 q/k/v, "
-                               "fp32 gates/state, chunk 64 + kda_decode_step B=256 H=96 d=128",
+                               "fp32 gates/state, chunk 32 + kda_decode_step B=256 H=96 d=128",
                    "prefill_tokens": T_tok, "heads": w_pre.heads, "head_dim": w_pre.head_dim,
                    "decode_sessions": w_dec.batch},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

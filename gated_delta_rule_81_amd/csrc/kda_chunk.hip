@@ -34,21 +34,23 @@
 //   * the diagonal tile (1,1) uses K+, Q+, K- of block 1 relative to rho.
 // Every factor is then bounded by e^{decay over 16 tokens}, so the numerics
 // contract (16-token decay sum > -80 per channel) keeps all of them finite.
-// K_end = K (.) e^{Gamma_last - Gamma} is formed as (K e^{rho - Gamma})
-// e^{Gamma_last - rho}, two factors in fp32 range.
+// K_end = K (.) e^{Gamma_last - Gamma} is applied as (K e^{rho - Gamma}),
+// stored in LDS, times the per-channel f = e^{Gamma_last - rho} in fp32 on the
+// scan side: both factors stay in fp32 range.
 //
 // Work split inside a workgroup.  D/16 preparation waves and DVS/16 scan
-// waves run in lockstep, three workgroup barriers per chunk: while the
+// waves run in lockstep, two workgroup barriers per chunk: while the
 // preparation waves build chunk n+1's operands, each scan wave advances its
 // 16 value columns of the state over chunk n.  Prepared operands are double
 // buffered in LDS.
 //   preparation, phase 1: cumulative log-decay (DPP lane scan), e^{+-Gamma}
 //                (v_exp_f32), operand tiles in LDS, next chunk's loads;
 //                phase 2: A and Tril(Q+ K-^T) (6 MFMA tiles), the diagonal
-//                blocks of T = (I + A)^{-1} by substitution;
-//                phase 3: the off-diagonal block of T (two MFMA products).
-//   scan, phase 1: [K+; Q+] S, X, Delta = T' X, O (stored);
-//         phase 2: S <- gamma S + Kend^T Delta.
+//                blocks T_00, T_11 of (I + A)^{-1} by substitution.
+//   scan, phase 1: [K+; Q+] S, X, Delta by block substitution
+//                (Delta_0 = T_00 b_0 X_0, Delta_1 = T_11 (b_1 X_1 - A_10 Delta_0)),
+//                O (stored);
+//         phase 2: S <- gamma S + f (K e^{rho - Gamma})^T Delta.
 // A scan wave keeps its state columns (all d_k rows) in fp32 MFMA
 // accumulators and feeds them straight back as the B operand of the next
 // chunk's products: the contraction index is permuted so that the
