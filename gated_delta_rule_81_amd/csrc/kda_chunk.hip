@@ -210,9 +210,17 @@ __device__ __forceinline__ void st8(float *p, const float (&f)[8]) {
     *reinterpret_cast<f32x4 *>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
 }
 
-// Registers holding one chunk's raw inputs for one preparation thread: one
-// token row, two runs of 4 channels of k, q and log_alpha; 16 bytes of the V
-// slice; one beta.
+// Four floats -> four consecutive T in LDS (8-byte aligned for bf16, 16 for fp32).
+__device__ __forceinline__ void st4(bf16 *p, const float (&f)[4]) {
+    *reinterpret_cast<u32x2 *>(p) = u32x2{pack2(f[0], f[1]), pack2(f[2], f[3])};
+}
+__device__ __forceinline__ void st4(float *p, const float (&f)[4]) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{f[0], f[1], f[2], f[3]};
+}
+
+// Registers holding one chunk's raw inputs for one preparation thread: a
+// run of 4 channels of k, q and log_alpha in token rows r and r + 16; 16
+// bytes of the V slice; one beta.
 template <typename T, int D, int DVS>
 struct ChunkRegs {
     typedef Cfg<T, D, DVS> G;
@@ -229,11 +237,12 @@ template <typename T, int D, int DVS>
 struct ChunkOffsets {
     typedef Cfg<T, D, DVS> G;
     int kq[2], g[2], v, b;
-    __device__ ChunkOffsets(int tid, int row, const int (&c)[2], int h, int H, int v0) {
+    __device__ ChunkOffsets(int tid, int row, int c, int h, int H, int v0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            kq[j] = ((row * H + h) * D + c[j]) * (int)sizeof(T);
-            g[j] = ((row * H + h) * D + c[j]) * 4;
+            const int rj = row + 16 * j;
+            kq[j] = ((rj * H + h) * D + c) * (int)sizeof(T);
+            g[j] = ((rj * H + h) * D + c) * 4;
         }
         const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
         v = ((vr * H + h) * D + v0 + vc) * (int)sizeof(T);
@@ -387,20 +396,13 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         T *sQD = reinterpret_cast<T *>(smem + G::oQD);
         T *sKM = reinterpret_cast<T *>(smem + G::oKM);
         float *sAt = reinterpret_cast<float *>(smem + G::oAt);
-        // thread map: token row r = lane % 32, physical channel block pb (8
-        // entries) = 2 wave + lane / 32, i.e. two runs of 4 logical channels
-        const int r = lane & 31;
-        const int pb = 2 * wave + (lane >> 5);
-        int crun[2];
-        if constexpr (sizeof(T) == 2) {
-            crun[0] = 32 * (pb >> 2) + 4 * (pb & 3);
-            crun[1] = crun[0] + 16;
-        } else {
-            crun[0] = 8 * pb;
-            crun[1] = crun[0] + 4;
-        }
-        const bool blk1 = r >= kBS;  // rows of block 1
-        const ChunkOffsets<T, D, DVS> offs(tid, r, crun, h, H, v0);
+        // thread map: token rows r (block 0) and r + 16 (block 1), r = lane % 16,
+        // so the 16 lanes of a DPP row are the 16 tokens of each block; logical
+        // channels c .. c + 3 (physical pc .. pc + 3), c = 4 (4 wave + lane / 16)
+        const int r = lane & 15;
+        const int c = 4 * (4 * wave + (lane >> 4));
+        const int pc = phys<T>(c);
+        const ChunkOffsets<T, D, DVS> offs(tid, r, c, h, H, v0);
         ChunkRegs<T, D, DVS> R;
         if (nchunks > 0)
             load_chunk(R, chunk_src(q, k, v, log_alpha, beta, tbeg,
@@ -423,79 +425,97 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 
             // ------------------------------------------------------ phase 1
             if (on) {
-                float kf[8], qf[8], d[8];
+                // block-relative inclusive prefix of the log2-gates (block 0's is
+                // chunk-relative); rho = Gamma_15 = block 0's total (lane 15)
+                float d0[4], d1[4], erho[4];
+                unpack<float, 4>(R.g[0], d0);
+                unpack<float, 4>(R.g[1], d1);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    unpack<T, 4>(R.k[j], kf + 4 * j);
-                    unpack<T, 4>(R.q[j], qf + 4 * j);
-                    unpack<float, 4>(R.g[j], d + 4 * j);
-                }
-                // block-relative inclusive prefix of the log2-gates: the 16
-                // lanes of a DPP row are the 16 tokens of one block
-                float erho[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float x = d[i] * kLog2e;
+                for (int e = 0; e < 4; ++e) {
+                    float x = d0[e] * kLog2e, y = d1[e] * kLog2e;
                     x += dpp_row_shr<1>(x);
+                    y += dpp_row_shr<1>(y);
                     x += dpp_row_shr<2>(x);
+                    y += dpp_row_shr<2>(y);
                     x += dpp_row_shr<4>(x);
+                    y += dpp_row_shr<4>(y);
                     x += dpp_row_shr<8>(x);
-                    d[i] = x;
-                    // rho = Gamma_15 (block 0's total): lane 15 of this row for
-                    // block 0, of the previous row for block 1
-                    const float own = dpp<0x15f, 0xf>(x);   // row_newbcast:15
-                    const float prev = dpp<0x142, 0xa>(x);  // row_bcast:15
-                    erho[i] = fast_exp2(blk1 ? prev : own);
+                    y += dpp_row_shr<8>(y);
+                    d0[e] = x;
+                    d1[e] = y;
+                    erho[e] = fast_exp2(dpp<0x15f, 0xf>(x));  // row_newbcast:15
                 }
-                float kt[8], ep[8];
+                float kf[4], qf[4];
+                float kt0[4], kt1[4], ep1[4];
                 {
-                    float kp[8], qp[8], km[8], kd[8], qd[8];
+                    // block 0: chunk-relative K+, Q+, K- and K e^{rho - Gamma}
+                    float kp[4], qp[4], km[4];
+                    unpack<T, 4>(R.k[0], kf);
+                    unpack<T, 4>(R.q[0], qf);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        ep[i] = fast_exp2(d[i]);
-                        const float em = fast_exp2(-d[i]);
-                        kd[i] = kf[i] * ep[i];  // block-relative (= chunk-relative in block 0)
-                        qd[i] = qf[i] * ep[i];
-                        const float sc = blk1 ? erho[i] : 1.f;
-                        kp[i] = kd[i] * sc;  // chunk-relative
-                        qp[i] = qd[i] * sc;
-                        km[i] = kf[i] * em;
-                        kt[i] = km[i] * (blk1 ? 1.f : erho[i]);  // K e^{rho - Gamma}
+                    for (int e = 0; e < 4; ++e) {
+                        const float ep = fast_exp2(d0[e]), em = fast_exp2(-d0[e]);
+                        kp[e] = kf[e] * ep;
+                        qp[e] = qf[e] * ep;
+                        km[e] = kf[e] * em;
+                        kt0[e] = km[e] * erho[e];
                     }
-                    st8(pKP + r * G::LDK + 8 * pb, kp);
-                    st8(pQP + r * G::LDK + 8 * pb, qp);
-                    st8(sKM + r * G::LDK + 8 * pb, km);
-                    if (blk1) {
-                        st8(sKD + (r - kBS) * G::LDK + 8 * pb, kd);
-                        st8(sQD + (r - kBS) * G::LDK + 8 * pb, qd);
-                    }
+                    st4(pKP + r * G::LDK + pc, kp);
+                    st4(pQP + r * G::LDK + pc, qp);
+                    st4(sKM + r * G::LDK + pc, km);
                 }
-                if (r == kC - 1) {
-                    // f1 = e^{Gamma_last - rho}, gamma = e^{Gamma_last}, two runs of 4
+                {
+                    // block 1: K+, Q+, K- relative to rho, chunk-relative K+, Q+
+                    float kd[4], qd[4], kp[4], qp[4];
+                    unpack<T, 4>(R.k[1], kf);
+                    unpack<T, 4>(R.q[1], qf);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        *reinterpret_cast<f32x4 *>(pF1 + crun[j]) =
-                            f32x4{ep[4 * j], ep[4 * j + 1], ep[4 * j + 2], ep[4 * j + 3]};
-                        *reinterpret_cast<f32x4 *>(pGam + crun[j]) =
-                            f32x4{erho[4 * j] * ep[4 * j], erho[4 * j + 1] * ep[4 * j + 1],
-                                  erho[4 * j + 2] * ep[4 * j + 2], erho[4 * j + 3] * ep[4 * j + 3]};
+                    for (int e = 0; e < 4; ++e) {
+                        ep1[e] = fast_exp2(d1[e]);
+                        const float em = fast_exp2(-d1[e]);
+                        kd[e] = kf[e] * ep1[e];
+                        qd[e] = qf[e] * ep1[e];
+                        kp[e] = kd[e] * erho[e];
+                        qp[e] = qd[e] * erho[e];
+                        kt1[e] = kf[e] * em;  // K- of block 1 = K e^{rho - Gamma}
                     }
+                    st4(pKP + (kBS + r) * G::LDK + pc, kp);
+                    st4(pQP + (kBS + r) * G::LDK + pc, qp);
+                    st4(sKM + (kBS + r) * G::LDK + pc, kt1);
+                    st4(sKD + r * G::LDK + pc, kd);
+                    st4(sQD + r * G::LDK + pc, qd);
                 }
-                // (K e^{rho - Gamma})^T, channel rows, token pairs: the even
-                // lane of a pair stores run 0 (channels 0-3), the odd lane run 1
+                if (r == kBS - 1) {
+                    // row 31: f = e^{Gamma_last - rho}, gamma = e^{Gamma_last}
+                    *reinterpret_cast<f32x4 *>(pF1 + c) = f32x4{ep1[0], ep1[1], ep1[2], ep1[3]};
+                    *reinterpret_cast<f32x4 *>(pGam + c) =
+                        f32x4{erho[0] * ep1[0], erho[1] * ep1[1], erho[2] * ep1[2],
+                              erho[3] * ep1[3]};
+                }
+                // (K e^{rho - Gamma})^T, channel rows, token pairs (r, r + 1) of
+                // both blocks: the even lane stores channels c, c + 1, the odd
+                // lane channels c + 2, c + 3
                 {
                     const bool odd = r & 1;
-                    T *dst = pKET + crun[odd ? 1 : 0] * G::LDT + phys<T>(r & ~1);
+                    const int tr = r & ~1;
+                    T *dst = pKET + (c + (odd ? 2 : 0)) * G::LDT;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float own = odd ? kt[4 + j] : kt[j];
-                        const float send = odd ? kt[j] : kt[4 + j];
-                        const float recv = dpp<0xb1, 0xf>(send);  // quad_perm [1,0,3,2]
-                        const float lo = odd ? recv : own, hi = odd ? own : recv;
-                        if constexpr (sizeof(T) == 2)
-                            *reinterpret_cast<unsigned *>(dst + j * G::LDT) = pack2(lo, hi);
-                        else
-                            *reinterpret_cast<f32x2 *>(dst + j * G::LDT) = f32x2{lo, hi};
+                    for (int b = 0; b < 2; ++b) {
+                        const float *kt = b ? kt1 : kt0;
+                        const int tcol = phys<T>(kBS * b + tr);
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float own = odd ? kt[e + 2] : kt[e];
+                            const float send = odd ? kt[e] : kt[e + 2];
+                            const float recv = dpp<0xb1, 0xf>(send);  // quad_perm [1,0,3,2]
+                            const float lo = odd ? recv : own, hi = odd ? own : recv;
+                            if constexpr (sizeof(T) == 2)
+                                *reinterpret_cast<unsigned *>(dst + e * G::LDT + tcol) =
+                                    pack2(lo, hi);
+                            else
+                                *reinterpret_cast<f32x2 *>(dst + e * G::LDT + tcol) =
+                                    f32x2{lo, hi};
+                        }
                     }
                 }
                 if (tid < G::VTH) {
