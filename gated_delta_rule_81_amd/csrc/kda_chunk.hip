@@ -93,7 +93,6 @@ struct Cfg {
     static constexpr int LDK = D + kPad;     // [token][channel] tiles
     static constexpr int LDT = kC + kPad;    // [*][token] tiles
     static constexpr int LDV = DVS + kPad;   // V slice rows
-    static constexpr int LDO = 16 + kPad;    // O staging rows (per scan wave)
     static constexpr int LDAT = kBS + 4;     // fp32 transposed diagonal blocks of A
     static constexpr int LDTT = kBS + kPad;  // 16x16 operand blocks of the substitution
     static constexpr int NRT = D / 16;       // d_k row tiles of the state
@@ -101,6 +100,14 @@ struct Cfg {
     static constexpr int VE = 16 / SZ;       // elements per 16-byte V access
     static constexpr int VTH = kC * DVS / VE;  // preparation threads that move the V slice
     static constexpr int RW = 4 * SZ / 4;    // words per 4-channel run of k / q
+    // whole-row loads: 16 bytes per lane, a row of k / q (RBK bytes), log_alpha
+    // (RBG) or the V slice (RBV) covered by RBX / 16 consecutive lanes
+    static constexpr int RBK = D * SZ, RBG = D * 4, RBV = DVS * SZ;
+    static constexpr int IK = RBK / 16 / 2 / PW;  // k (and q) load instructions per wave
+    static constexpr int IG = RBG / 16 / 2 / PW;  // log_alpha load instructions per wave
+    static constexpr int NIV = RBV / 16 / 2;      // V load instructions (waves 0 .. NIV-1)
+    static constexpr int IO = RBV / 16 / 2 / SWV; // O store instructions per scan wave
+    static constexpr int LSK = RBK + 16, LSG = RBG + 16, LSV = RBV + 16;  // staging row bytes
 
     // one buffer set of prepared operands (byte offsets inside the set)
     static constexpr int B_TK = kC * LDK * SZ;
@@ -113,15 +120,21 @@ struct Cfg {
     // preparation scratch
     static constexpr int oKD = 2 * SET, oQD = oKD + kBS * LDK * SZ, oKM = oQD + kBS * LDK * SZ,
                          oAt = oKM + B_TK;
-    // scan scratch: O staging, one region per scan wave
-    static constexpr int oO = oAt + 2 * kBS * LDAT * 4, BYTES = oO + SWV * kC * LDO * SZ;
+    // staging of the next chunk's raw rows (k, q, log_alpha, V slice, beta)
+    static constexpr int oRK = oAt + 2 * kBS * LDAT * 4, oRQ = oRK + kC * LSK,
+                         oRG = oRQ + kC * LSK, oRV = oRG + kC * LSG, oRB = oRV + kC * LSV;
+    // O staging (all scan waves), stored as whole rows in the next phase
+    static constexpr int oO = oRB + kC * 4, BYTES = oO + kC * LSV;
 
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(DVS % 16 == 0 && D % DVS == 0, "d_v slice");
     static_assert(VTH <= PW * 64 && VTH >= kC, "V slice map");
     static_assert(D % KB == 0, "state contraction blocks");
-    static_assert(SET % 16 == 0 && oKM % 16 == 0 && oAt % 16 == 0 && oO % 16 == 0,
-                  "16-byte alignment");
+    static_assert(IK >= 1 && IG >= 1 && IO >= 1 && NIV <= PW &&
+                      IK * PW * 2 * 16 == RBK && IG * PW * 2 * 16 == RBG &&
+                      IO * SWV * 2 * 16 == RBV, "whole-row load maps");
+    static_assert(SET % 16 == 0 && oKM % 16 == 0 && oAt % 16 == 0 && oO % 16 == 0 &&
+                      oRK % 16 == 0 && oRG % 16 == 0 && oRV % 16 == 0, "16-byte alignment");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -218,50 +231,79 @@ __device__ __forceinline__ void st4(float *p, const float (&f)[4]) {
     *reinterpret_cast<f32x4 *>(p) = f32x4{f[0], f[1], f[2], f[3]};
 }
 
-// Registers holding one chunk's raw inputs for one preparation thread: a
-// run of 4 channels of k, q and log_alpha in token rows r and r + 16; 16
-// bytes of the V slice; one beta.
+// One chunk's raw inputs in flight for one preparation thread, loaded as
+// whole rows (16 bytes per lane, consecutive lanes along a row): IK pieces
+// each of k and q, IG of log_alpha, one of the V slice (last NIV waves), one
+// beta (last wave).  Waves 0 and 1 run the triangular solves, so the extra
+// pieces go to the other waves.
 template <typename T, int D, int DVS>
 struct ChunkRegs {
     typedef Cfg<T, D, DVS> G;
-    Raw<G::RW> k[2], q[2];
-    Raw<4> g[2];
-    Raw<4> v;
+    Raw<4> k[G::IK], q[G::IK], g[G::IG], v;
     float beta;
 };
 
-// Byte offsets (relative to a chunk's first token) of a preparation
-// thread's loads; loop-invariant, so each chunk only rebuilds the scalar
-// descriptors.
+// Where a preparation thread's pieces come from (byte offsets relative to a
+// chunk's first token; loop-invariant) and where they go in the staging area.
 template <typename T, int D, int DVS>
 struct ChunkOffsets {
     typedef Cfg<T, D, DVS> G;
-    int kq[2], g[2], v, b;
-    __device__ ChunkOffsets(int tid, int row, int c, int h, int H, int v0) {
+    int gk[G::IK], sk[G::IK], gg[G::IG], sg[G::IG], gv, sv, gb;
+    __device__ ChunkOffsets(int wave, int lane, int h, int H, int v0) {
+        constexpr int LK = G::RBK / 16, LG = G::RBG / 16, LV = G::RBV / 16;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int rj = row + 16 * j;
-            kq[j] = ((rj * H + h) * D + c) * (int)sizeof(T);
-            g[j] = ((rj * H + h) * D + c) * 4;
+        for (int i = 0; i < G::IK; ++i) {
+            const int p = (wave * G::IK + i) * 64 + lane, row = p / LK, b = 16 * (p % LK);
+            gk[i] = (row * H + h) * G::RBK + b;
+            sk[i] = row * G::LSK + b;
         }
-        const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
-        v = ((vr * H + h) * D + v0 + vc) * (int)sizeof(T);
-        b = (tid * H + h) * 4;
+#pragma unroll
+        for (int i = 0; i < G::IG; ++i) {
+            const int p = (wave * G::IG + i) * 64 + lane, row = p / LG, b = 16 * (p % LG);
+            gg[i] = (row * H + h) * G::RBG + b;
+            sg[i] = row * G::LSG + b;
+        }
+        const int p = (wave - (G::PW - G::NIV)) * 64 + lane, row = p / LV, b = 16 * (p % LV);
+        gv = ((row * H + h) * D + v0) * (int)sizeof(T) + b;
+        sv = row * G::LSV + b;
+        gb = (lane * H + h) * 4;
     }
 };
 
 template <typename T, int D, int DVS>
 __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
-                                           const ChunkOffsets<T, D, DVS> &o, int tid) {
+                                           const ChunkOffsets<T, D, DVS> &o, int wave,
+                                           int lane) {
     typedef Cfg<T, D, DVS> G;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        R.k[j] = buf_load<G::RW>(s.k, o.kq[j]);
-        R.q[j] = buf_load<G::RW>(s.q, o.kq[j]);
-        R.g[j] = buf_load<4>(s.g, o.g[j]);
+    for (int i = 0; i < G::IK; ++i) {
+        R.k[i] = buf_load<4>(s.k, o.gk[i]);
+        R.q[i] = buf_load<4>(s.q, o.gk[i]);
     }
-    if (tid < G::VTH) R.v = buf_load<4>(s.v, o.v);
-    if (tid < kC) R.beta = __uint_as_float(buf_load<1>(s.b, o.b).w[0]);
+#pragma unroll
+    for (int i = 0; i < G::IG; ++i) R.g[i] = buf_load<4>(s.g, o.gg[i]);
+    if (wave >= G::PW - G::NIV) R.v = buf_load<4>(s.v, o.gv);
+    if (wave == G::PW - 1 && lane < kC) R.beta = __uint_as_float(buf_load<1>(s.b, o.gb).w[0]);
+}
+
+// The pieces into the staging area (waits for the loads to land).
+template <typename T, int D, int DVS>
+__device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS> &R, unsigned char *smem,
+                                            const ChunkOffsets<T, D, DVS> &o, int wave,
+                                            int lane) {
+    typedef Cfg<T, D, DVS> G;
+    auto st16 = [](unsigned char *p, const Raw<4> &x) {
+        *reinterpret_cast<u32x4 *>(p) = u32x4{x.w[0], x.w[1], x.w[2], x.w[3]};
+    };
+#pragma unroll
+    for (int i = 0; i < G::IK; ++i) {
+        st16(smem + G::oRK + o.sk[i], R.k[i]);
+        st16(smem + G::oRQ + o.sk[i], R.q[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < G::IG; ++i) st16(smem + G::oRG + o.sg[i], R.g[i]);
+    if (wave >= G::PW - G::NIV) st16(smem + G::oRV + o.sv, R.v);
+    if (wave == G::PW - 1 && lane < kC) reinterpret_cast<float *>(smem + G::oRB)[lane] = R.beta;
 }
 
 // DPP helpers (all lanes active).
@@ -402,12 +444,14 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         const int r = lane & 15;
         const int c = 4 * (4 * wave + (lane >> 4));
         const int pc = phys<T>(c);
-        const ChunkOffsets<T, D, DVS> offs(tid, r, c, h, H, v0);
+        const ChunkOffsets<T, D, DVS> offs(wave, lane, h, H, v0);
         ChunkRegs<T, D, DVS> R;
-        if (nchunks > 0)
+        if (nchunks > 0) {
             load_chunk(R, chunk_src(q, k, v, log_alpha, beta, tbeg,
                                     (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D),
-                       offs, tid);
+                       offs, wave, lane);
+            stage_chunk(R, smem, offs, wave, lane);
+        }
         __syncthreads();
 
         for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
@@ -425,11 +469,53 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 
             // ------------------------------------------------------ phase 1
             if (on) {
+                // the next chunk's loads go out first: they land while this chunk
+                // is prepared and are staged at the end of phase 2
+                if (tick + 1 < nchunks) {
+                    const int64_t ntok0 = tbeg + (int64_t)(tick + 1) * kC;
+                    load_chunk(R, chunk_src(q, k, v, log_alpha, beta, ntok0,
+                                            (int)((tend - ntok0) < kC ? (tend - ntok0) : kC), H,
+                                            D),
+                               offs, wave, lane);
+                }
+                // this chunk's rows r and r + 16 from the staging area
+                Raw<G::RW> rk[2], rq[2];
+                Raw<4> rg[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int row = r + kBS * j;
+                    if constexpr (G::RW == 2) {
+                        const u32x2 a = *reinterpret_cast<const u32x2 *>(
+                            smem + G::oRK + row * G::LSK + c * G::SZ);
+                        const u32x2 b = *reinterpret_cast<const u32x2 *>(
+                            smem + G::oRQ + row * G::LSK + c * G::SZ);
+                        rk[j].w[0] = a[0]; rk[j].w[1] = a[1];
+                        rq[j].w[0] = b[0]; rq[j].w[1] = b[1];
+                    } else {
+                        const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                            smem + G::oRK + row * G::LSK + c * G::SZ);
+                        const u32x4 b = *reinterpret_cast<const u32x4 *>(
+                            smem + G::oRQ + row * G::LSK + c * G::SZ);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) { rk[j].w[i] = a[i]; rq[j].w[i] = b[i]; }
+                    }
+                    const u32x4 gg = *reinterpret_cast<const u32x4 *>(
+                        smem + G::oRG + row * G::LSG + c * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rg[j].w[i] = gg[i];
+                }
+                if (tid < G::VTH) {
+                    const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
+                    *reinterpret_cast<u32x4 *>(pV + vr * G::LDV + vc) =
+                        *reinterpret_cast<const u32x4 *>(smem + G::oRV + vr * G::LSV +
+                                                         vc * G::SZ);
+                }
+                if (tid < kC) pBeta[tid] = reinterpret_cast<const float *>(smem + G::oRB)[tid];
                 // block-relative inclusive prefix of the log2-gates (block 0's is
                 // chunk-relative); rho = Gamma_15 = block 0's total (lane 15)
                 float d0[4], d1[4], erho[4];
-                unpack<float, 4>(R.g[0], d0);
-                unpack<float, 4>(R.g[1], d1);
+                unpack<float, 4>(rg[0], d0);
+                unpack<float, 4>(rg[1], d1);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float x = d0[e] * kLog2e, y = d1[e] * kLog2e;
@@ -450,8 +536,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 {
                     // block 0: chunk-relative K+, Q+, K- and K e^{rho - Gamma}
                     float kp[4], qp[4], km[4];
-                    unpack<T, 4>(R.k[0], kf);
-                    unpack<T, 4>(R.q[0], qf);
+                    unpack<T, 4>(rk[0], kf);
+                    unpack<T, 4>(rq[0], qf);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float ep = fast_exp2(d0[e]), em = fast_exp2(-d0[e]);
@@ -467,8 +553,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 {
                     // block 1: K+, Q+, K- relative to rho, chunk-relative K+, Q+
                     float kd[4], qd[4], kp[4], qp[4];
-                    unpack<T, 4>(R.k[1], kf);
-                    unpack<T, 4>(R.q[1], qf);
+                    unpack<T, 4>(rk[1], kf);
+                    unpack<T, 4>(rq[1], qf);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         ep1[e] = fast_exp2(d1[e]);
@@ -518,19 +604,6 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                         }
                     }
                 }
-                if (tid < G::VTH) {
-                    const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
-                    *reinterpret_cast<u32x4 *>(pV + vr * G::LDV + vc) =
-                        u32x4{R.v.w[0], R.v.w[1], R.v.w[2], R.v.w[3]};
-                }
-                if (tid < kC) pBeta[tid] = R.beta;
-                // the registers are free: start loading the next chunk
-                const int64_t ntok0 = tbeg + (int64_t)(tick + 1) * kC;
-                if (tick + 1 < nchunks)
-                    load_chunk(R, chunk_src(q, k, v, log_alpha, beta, ntok0,
-                                            (int)((tend - ntok0) < kC ? (tend - ntok0) : kC), H,
-                                            D),
-                               offs, tid);
             }
             __syncthreads();
 
@@ -612,6 +685,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                         dstT[(4 * g + e) * G::LDTT + j] = from_f32<T>(s[e] * bj);
                 }
             }
+            // the next chunk's rows, loaded during phase 1, into the staging area
+            if (tick + 1 < nchunks) stage_chunk(R, smem, offs, wave, lane);
             __syncthreads();
 
         }
@@ -623,7 +698,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     // d_k rows: NRT fp32 accumulator tiles (lane: value column 16 ct + l16,
     // key rows 16 t + 4 l4 + e)
     const int ct = wave - G::PW;
-    T *sO = reinterpret_cast<T *>(smem + G::oO) + ct * kC * G::LDO;
+    T *sO = reinterpret_cast<T *>(smem + G::oO);  // [kC][LSV bytes], all scan waves
     const int64_t sbase = ((int64_t)n * H + h) * D * D;  // M = S^T: [d_v][d_k]
     const int vcol = v0 + 16 * ct + l16;
     f32x4 Sm[G::NRT];
@@ -647,11 +722,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         const float *cGam = reinterpret_cast<const float *>(SS + G::sGam);
         const float *cF1 = reinterpret_cast<const float *>(SS + G::sF1);
         f32x4 Dl[2];  // Delta row tiles (tokens 0-15, 16-31), kept for phase 2
+        const int64_t tok0 = tbeg + (int64_t)(tick - 1) * kC;
+        const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
 
         // ---------------------------------------------------------- phase 1
         if (on) {
-            const int64_t tok0 = tbeg + (int64_t)(tick - 1) * kC;
-            const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
             // the state as B operands, one per contraction block
             typename SM::Frag Sb[D / G::KB];
 #pragma unroll
@@ -704,24 +779,26 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 1, lane), Db1);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sO[(kBS * rt + 4 * l4 + e) * G::LDO + l16] = from_f32<T>(PQ[rt][e]);
-            }
-            wave_lds_fence();
-            // 32 rows x 16 columns of O, 16-byte pieces
-            constexpr int PPR = 16 * (int)sizeof(T) / 16;  // pieces per row
-#pragma unroll
-            for (int p = lane; p < kC * PPR; p += 64) {
-                const int orow = p / PPR, opc = (p % PPR) * G::VE;
-                if (orow < nvalid)
-                    *reinterpret_cast<u32x4 *>(out + ((tok0 + orow) * H + h) * (int64_t)D + v0 +
-                                               16 * ct + opc) =
-                        *reinterpret_cast<const u32x4 *>(sO + orow * G::LDO + opc);
+                    sO[(kBS * rt + 4 * l4 + e) * (G::LSV / G::SZ) + 16 * ct + l16] =
+                        from_f32<T>(PQ[rt][e]);
             }
         }
         __syncthreads();
 
         // ---------------------------------------------------------- phase 2
         if (on) {
+            // the chunk's O rows (32 x DVS), whole rows in 16-byte pieces
+            constexpr int LV = G::RBV / 16;
+#pragma unroll
+            for (int i = 0; i < G::IO; ++i) {
+                const int p = (ct * G::IO + i) * 64 + lane, orow = p / LV, b = 16 * (p % LV);
+                if (orow < nvalid)
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(
+                                                   out + ((tok0 + orow) * H + h) * (int64_t)D +
+                                                   v0) + b) =
+                        *reinterpret_cast<const u32x4 *>(
+                            reinterpret_cast<const unsigned char *>(sO) + orow * G::LSV + b);
+            }
             // S <- Diag(gamma) S + Diag(f1) (K e^{rho - Gamma})^T Delta
             const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
             const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
