@@ -504,13 +504,6 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) rg[j].w[i] = gg[i];
                 }
-                if (tid < G::VTH) {
-                    const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
-                    *reinterpret_cast<u32x4 *>(pV + vr * G::LDV + vc) =
-                        *reinterpret_cast<const u32x4 *>(smem + G::oRV + vr * G::LSV +
-                                                         vc * G::SZ);
-                }
-                if (tid < kC) pBeta[tid] = reinterpret_cast<const float *>(smem + G::oRB)[tid];
                 // block-relative inclusive prefix of the log2-gates (block 0's is
                 // chunk-relative); rho = Gamma_15 = block 0's total (lane 15)
                 float d0[4], d1[4], erho[4];
@@ -604,6 +597,15 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                         }
                     }
                 }
+                // V slice and beta copies last: their LDS round trips stay off
+                // the path of the elementwise work
+                if (tid < G::VTH) {
+                    const int vr = tid / (DVS / G::VE), vc = G::VE * (tid % (DVS / G::VE));
+                    *reinterpret_cast<u32x4 *>(pV + vr * G::LDV + vc) =
+                        *reinterpret_cast<const u32x4 *>(smem + G::oRV + vr * G::LSV +
+                                                         vc * G::SZ);
+                }
+                if (tid < kC) pBeta[tid] = reinterpret_cast<const float *>(smem + G::oRB)[tid];
             }
             __syncthreads();
 
