@@ -75,10 +75,10 @@ enum kda_status {
 
 /*
  * kda_chunk_fwd -- prefill: the KDA recurrence over whole sequences, computed
- * chunkwise ("recurrence between chunks, parallel work inside each chunk",
- * [K3-explainer] §六.1) through the WY/UT representation of the chunk's
+ * chunkwise: sequential from chunk to chunk, parallel inside a chunk
+ * ([K3-explainer] §六.1), through the WY/UT representation of the chunk's
  * rank-one updates ([K3-explainer] §六.2).  The result equals the token-by-
- * token recurrence up to floating-point rounding; the chunk length (64) only
+ * token recurrence up to floating-point rounding; the chunk length (32) only
  * affects speed.
  *
  * Layout (dense, cu_seqlens == NULL): B = batch sequences of T = seq_len
