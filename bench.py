@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="time kda_chunk_fwd only (for counter passes); no decode fields")
+    ap.add_argument("--snapshot-every", type=int, default=0,
+                    help="time kda_chunk_fwd_snapshots with a state snapshot every N tokens "
+                         "(a multiple of 32) instead of kda_chunk_fwd")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
@@ -150,11 +153,23 @@ def main():
     fin = torch.empty_like(P["initial_state"])
     dout = torch.empty((w_dec.batch, w_dec.heads, w_dec.head_dim), dtype=torch.bfloat16,
                        device=dev)
+    every = args.snapshot_every
+    n_snap = w_pre.batch * (w_pre.seq_len // every) if every > 0 else 0
+    snaps = (torch.empty((n_snap, w_pre.heads, w_pre.head_dim, w_pre.head_dim),
+                         dtype=torch.float32, device=dev) if every > 0 else None)
     torch.cuda.synchronize()
 
+    def prefill():
+        if every > 0:
+            kda.chunk_fwd_snapshots(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], every,
+                                    P["initial_state"], out=out, final_state=fin,
+                                    snapshots=snaps)
+        else:
+            kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"],
+                          P["initial_state"], out=out, final_state=fin)
+
     def step(s):
-        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["initial_state"],
-                      out=out, final_state=fin)
+        prefill()
         t = s % w_dec.steps
         kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
                         state, out=dout)
@@ -173,8 +188,7 @@ def main():
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
-        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["initial_state"],
-                      out=out, final_state=fin)
+        prefill()
         e[1].record(stream)
         t = (args.warmup + s) % w_dec.steps
         kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
@@ -200,11 +214,12 @@ def main():
 
     T_tok = w_pre.batch * w_pre.seq_len
     pbytes = prefill_bytes(T_tok, w_pre.heads, w_pre.head_dim, w_pre.batch)
+    pbytes += n_snap * w_pre.heads * w_pre.head_dim * w_pre.head_dim * 4  # snapshot writes
     dbytes = decode_bytes(w_dec.batch, w_dec.heads, w_dec.head_dim)
     pre_gbs = pbytes / (pre_avg * 1e-3) / 1e9
     dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic() if every == 0 else None
 
     result = {
         "metric": "KDA chunked-fwd tokens/s (H=96,d=128,T=32K); decode state-update HBM GB/s",
@@ -219,8 +234,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "kda_chunk_fwd B=1 H=96 T=32768 d_k=d_v=128 bf16 q/k/v, "
+        "config": {"workload": ("kda_chunk_fwd" if every == 0 else
+                                f"kda_chunk_fwd_snapshots (every {every} tokens)")
+                               + " B=1 H=96 T=32768 d_k=d_v=128 bf16 q/k/v, "
                                "fp32 gates/state, chunk 32 + kda_decode_step B=256 H=96 d=128",
+                   "snapshot_every": every or None,
                    "prefill_tokens": T_tok, "heads": w_pre.heads, "head_dim": w_pre.head_dim,
                    "decode_sessions": w_dec.batch},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -3,9 +3,10 @@
 Python front end of ``libkda.so``; the C ABI is declared in include/kda.h.
 
     out, final_state = chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens)
+    out, final_state, snapshots = chunk_fwd_snapshots(q, k, v, log_alpha, beta, every)
     out = decode_step(q, k, v, log_alpha, beta, state)   # state updated in place
 """
 from ._lib import KdaError, lib
-from .ops import chunk_fwd, decode_step
+from .ops import chunk_fwd, chunk_fwd_snapshots, decode_step
 
-__all__ = ["chunk_fwd", "decode_step", "KdaError", "lib"]
+__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "decode_step", "KdaError", "lib"]

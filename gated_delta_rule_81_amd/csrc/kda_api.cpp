@@ -67,47 +67,63 @@ const char *kda_status_string(int status) {
     }
 }
 
-int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
-                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                  void *out, float *final_state, int32_t batch, int32_t seq_len,
-                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
-                  int32_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by kda_chunk_fwd and kda_chunk_fwd_snapshots (snapshots == NULL and
+// num_snapshots == 0 for the former).
+int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                   void *out, float *final_state, float *snapshots, int32_t snapshot_every,
+                   int32_t num_snapshots, int32_t batch, int32_t seq_len, int32_t num_heads,
+                   int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs, int32_t dtype,
+                   hipStream_t stream) {
     // sizes
     if (batch < 0 || seq_len < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0)
         return KDA_ERR_SHAPE;
+    if (num_snapshots < 0) return KDA_ERR_SHAPE;
+    const bool snap = snapshots != nullptr || num_snapshots > 0;
+    if (snap && snapshot_every <= 0) return KDA_ERR_SHAPE;
     if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
     const bool packed = cu_seqlens != nullptr;
     if (packed && (batch != 1 || num_seqs < 0)) return KDA_ERR_SHAPE;
     const int64_t tokens = (int64_t)batch * seq_len;
     if (tokens > INT32_MAX) return KDA_ERR_SHAPE;
     const int64_t nseq = packed ? num_seqs : batch;
+    // dense: every sequence has seq_len tokens, so the count is known here
+    if (snap && !packed && (int64_t)batch * (seq_len / snapshot_every) > num_snapshots)
+        return KDA_ERR_SHAPE;
     const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
     const uint64_t th = (uint64_t)tokens * num_heads;
     // pointers required whenever the array they describe is not empty
     const bool have_tokens = th > 0;
     if (have_tokens && (!q || !k || !v || !log_alpha || !beta || !out)) return KDA_ERR_NULL;
+    if (num_snapshots > 0 && num_heads > 0 && !snapshots) return KDA_ERR_NULL;
     // supported configurations
     if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
     const int d = head_dim_k;
     if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
     if (dtype == kda::kDtypeF32 && d != 64) return KDA_ERR_UNSUPPORTED;
+    if (snap && snapshot_every % kda::kChunkTokens != 0) return KDA_ERR_UNSUPPORTED;
     // the kernel addresses 64 tokens of one tensor with 32-bit byte offsets
     if ((int64_t)num_heads * d * 4 * 64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     // alignment
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
         !aligned4(beta) || !aligned16(initial_state) || !aligned16(out) ||
-        !aligned16(final_state) || !aligned4(cu_seqlens))
+        !aligned16(final_state) || !aligned4(cu_seqlens) || !aligned16(snapshots))
         return KDA_ERR_ALIGN;
     // aliasing
     const uint64_t state_bytes = (uint64_t)nseq * num_heads * d * d * 4;
     const Range rq{q, th * d * esz}, rk{k, th * d * esz}, rv{v, th * d * esz},
         rg{log_alpha, th * d * 4}, rb{beta, th * 4}, rs0{initial_state, state_bytes},
         rcu{cu_seqlens, packed ? (uint64_t)(nseq + 1) * 4 : 0}, ro{out, th * d * esz},
-        rs1{final_state, state_bytes};
+        rs1{final_state, state_bytes},
+        rsn{snapshots, (uint64_t)num_snapshots * num_heads * d * d * 4};
     const Range inputs[] = {rq, rk, rv, rg, rb, rs0, rcu};
     for (const Range &r : inputs)
-        if (overlap(ro, r)) return KDA_ERR_ALIAS;
-    if (overlap(ro, rs1)) return KDA_ERR_ALIAS;
+        if (overlap(ro, r) || overlap(rsn, r)) return KDA_ERR_ALIAS;
+    if (overlap(ro, rs1) || overlap(rsn, ro) || overlap(rsn, rs1)) return KDA_ERR_ALIAS;
     for (int i = 0; i < 7; ++i) {
         if (i == 5 && final_state && (const void *)final_state == (const void *)initial_state)
             continue;  // in-place state update is allowed
@@ -117,9 +133,37 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_
     const int st = check_device();
     if (st != KDA_OK) return st;
     const int rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                         final_state, (int32_t)nseq, seq_len, (int32_t)tokens,
-                                         num_heads, d, dtype, stream);
+                                         final_state, num_snapshots > 0 ? snapshots : nullptr,
+                                         snapshot_every, num_snapshots, (int32_t)nseq, seq_len,
+                                         (int32_t)tokens, num_heads, d, dtype, stream);
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  void *out, float *final_state, int32_t batch, int32_t seq_len,
+                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
+                  int32_t dtype, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state,
+                          nullptr, 0, 0, batch, seq_len, num_heads, head_dim_k, head_dim_v,
+                          num_seqs, dtype, stream);
+}
+
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, const float *initial_state,
+                            const int32_t *cu_seqlens, void *out, float *final_state,
+                            float *snapshots, int32_t snapshot_every, int32_t num_snapshots,
+                            int32_t batch, int32_t seq_len, int32_t num_heads,
+                            int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
+                            int32_t dtype, hipStream_t stream) {
+    if (snapshot_every <= 0) return KDA_ERR_SHAPE;
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state,
+                          snapshots, snapshot_every, num_snapshots, batch, seq_len, num_heads,
+                          head_dim_k, head_dim_v, num_seqs, dtype, stream);
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,

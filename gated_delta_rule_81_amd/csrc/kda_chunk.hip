@@ -64,7 +64,7 @@ namespace kda {
 
 namespace {
 
-constexpr int kC = 32;   // chunk length
+constexpr int kC = kChunkTokens;  // chunk length
 constexpr int kBS = 16;  // block / tile size
 
 // Physical position of contraction index i (a key channel or a token) in
@@ -383,8 +383,9 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
-    T *__restrict__ out, float *__restrict__ final_state, int num_seqs, int seq_len,
-    int total_tokens, int H, int units, int units_per_xcd) {
+    T *__restrict__ out, float *__restrict__ final_state, float *__restrict__ snapshots,
+    int snap_every, int snap_cap, int num_seqs, int seq_len, int total_tokens, int H, int units,
+    int units_per_xcd) {
     typedef Cfg<T, D, DVS> G;
     typedef Mma<T> M;
     typedef ScanMma<T> SM;
@@ -702,6 +703,27 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const int ct = wave - G::PW;
     T *sO = reinterpret_cast<T *>(smem + G::oO);  // [kC][LSV bytes], all scan waves
     const int64_t sbase = ((int64_t)n * H + h) * D * D;  // M = S^T: [d_v][d_k]
+    // State snapshots: the state after the first j * snap_every tokens of this
+    // sequence goes to entry snap_base + j - 1 of [snap_cap, H, d_v, d_k], where
+    // snap_base counts the snapshots of the sequences before it (their lengths
+    // clamped exactly as their own workgroups clamp them).
+    int snap_base = 0;
+    if (snapshots) {
+        if (cu_seqlens) {
+            int cnt = 0;
+            for (int m = lane; m < n; m += 64) {
+                int a = cu_seqlens[m], b = cu_seqlens[m + 1];
+                a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+                b = b < a ? a : (b > total_tokens ? total_tokens : b);
+                cnt += (b - a) / snap_every;
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+            snap_base = cnt;
+        } else {
+            snap_base = n * (seq_len / snap_every);
+        }
+    }
     const int vcol = v0 + 16 * ct + l16;
     f32x4 Sm[G::NRT];
 #pragma unroll
@@ -814,6 +836,18 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sm[t][e] = gm[e] * Sm[t][e] + f1[e] * acc[e];
             }
+            // a snapshot after every snap_every tokens (a multiple of the chunk
+            // length, so only full chunks end on one)
+            const int64_t done = (int64_t)tick * kC;
+            if (snapshots && done % snap_every == 0 && done <= tend - tbeg) {
+                const int64_t idx = snap_base + done / snap_every - 1;
+                if (idx < snap_cap) {
+                    float *dst = snapshots + (idx * H + h) * D * D + (int64_t)vcol * D + 4 * l4;
+#pragma unroll
+                    for (int t = 0; t < G::NRT; ++t)
+                        *reinterpret_cast<f32x4 *>(dst + 16 * t) = Sm[t];
+                }
+            }
         }
         __syncthreads();
     }
@@ -829,7 +863,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 template <typename T, int D, int DVS>
 int launch(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
            const float *initial_state, const int32_t *cu_seqlens, void *out, float *final_state,
-           int num_seqs, int seq_len, int total_tokens, int H, hipStream_t stream) {
+           float *snapshots, int snap_every, int snap_cap, int num_seqs, int seq_len,
+           int total_tokens, int H, hipStream_t stream) {
     const int64_t units64 = (int64_t)num_seqs * H * (D / DVS);
     if (units64 == 0) return 0;
     if (units64 > (int64_t)1 << 30) return -1;
@@ -838,8 +873,8 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
     hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS>), dim3(8 * per_xcd),
                        dim3(Cfg<T, D, DVS>::THREADS), 0, stream, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
-                       initial_state, cu_seqlens, static_cast<T *>(out), final_state, num_seqs,
-                       seq_len, total_tokens, H, units, per_xcd);
+                       initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,
+                       snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -847,20 +882,23 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
 
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                     void *out, float *final_state, int32_t num_seqs, int32_t seq_len,
+                     void *out, float *final_state, float *snapshots, int32_t snapshot_every,
+                     int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
                      hipStream_t stream) {
+    if (!snapshots) snapshot_every = kC, num_snapshots = 0;
     if (dtype == kDtypeBf16) {
         if (head_dim == 128)
             return launch<bf16, 128, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                         final_state, num_seqs, seq_len, total_tokens, num_heads,
-                                         stream);
+                                         final_state, snapshots, snapshot_every, num_snapshots,
+                                         num_seqs, seq_len, total_tokens, num_heads, stream);
         return launch<bf16, 64, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                    final_state, num_seqs, seq_len, total_tokens, num_heads,
-                                    stream);
+                                    final_state, snapshots, snapshot_every, num_snapshots,
+                                    num_seqs, seq_len, total_tokens, num_heads, stream);
     }
     return launch<float, 64, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                 final_state, num_seqs, seq_len, total_tokens, num_heads, stream);
+                                 final_state, snapshots, snapshot_every, num_snapshots, num_seqs,
+                                 seq_len, total_tokens, num_heads, stream);
 }
 
 }  // namespace kda

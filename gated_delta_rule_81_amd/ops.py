@@ -88,6 +88,71 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     return out, final_state
 
 
+def chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        log_alpha: torch.Tensor, beta: torch.Tensor, snapshot_every: int,
+                        initial_state: Optional[torch.Tensor] = None,
+                        cu_seqlens: Optional[torch.Tensor] = None, *,
+                        num_snapshots: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        snapshots: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor], torch.Tensor]:
+    """``chunk_fwd`` that also returns the state after every ``snapshot_every``
+    tokens of each sequence (``kda_chunk_fwd_snapshots``; [K3-memory] §5).
+
+    Returns (out, final_state, snapshots [S, H, d_v, d_k] fp32): the snapshots
+    of all sequences in sequence order, each sequence's in token order, S =
+    sum over sequences of floor(length / snapshot_every).  For packed input
+    the count needs the lengths: pass ``num_snapshots``, or it is computed from
+    a host copy of ``cu_seqlens`` (a device synchronisation).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    every = int(snapshot_every)
+    if every <= 0:
+        raise ValueError("snapshot_every must be positive")
+    _expect(q, "q", q.dtype, (B, T, H, dk), dev)
+    _expect(k, "k", q.dtype, (B, T, H, dk), dev)
+    _expect(v, "v", q.dtype, (B, T, H, dv), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    _expect(beta, "beta", torch.float32, (B, T, H), dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be 1-D")
+        _expect(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev)
+        N = cu_seqlens.shape[0] - 1
+        if num_snapshots is None:
+            lengths = cu_seqlens.to("cpu", torch.int64)
+            num_snapshots = int(((lengths[1:] - lengths[:-1]) // every).sum())
+    else:
+        N = B
+        if num_snapshots is None:
+            num_snapshots = B * (T // every)
+    _expect(initial_state, "initial_state", torch.float32, (N, H, dv, dk), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _expect(out, "out", q.dtype, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    _expect(final_state, "final_state", torch.float32, (N, H, dv, dk), dev)
+    if snapshots is None:
+        snapshots = torch.empty((num_snapshots, H, dv, dk), dtype=torch.float32, device=dev)
+    _expect(snapshots, "snapshots", torch.float32, (num_snapshots, H, dv, dk), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_chunk_fwd_snapshots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _ptr(snapshots), every, num_snapshots,
+        B, T, H, dk, dv, N if cu_seqlens is not None else 0, _DTYPES[q.dtype], stream)
+    check(rc, "kda_chunk_fwd_snapshots")
+    return out, final_state, snapshots
+
+
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
                 beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None
                 ) -> torch.Tensor:

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -108,6 +108,45 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_
                   void *out, float *final_state, int32_t batch, int32_t seq_len,
                   int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
                   int32_t dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also keeps the recurrent state
+ * at regular points of each sequence: restartable checkpoints and the state
+ * blocks a prefix cache stores, since a KDA state depends on its whole prefix
+ * and cannot be assembled from pieces the way paged KV blocks can
+ * ([K3-memory] §5: one state snapshot every 20,000 tokens of a 1M-token run).
+ *
+ * Every argument shared with kda_chunk_fwd has the same meaning, layout and
+ * rules.  In addition, for each sequence n (dense: each batch row) of length
+ * L_n, the state after its first j * snapshot_every tokens, for
+ * j = 1 .. floor(L_n / snapshot_every), is written (fp32, stored transposed
+ * like every state) to entry base_n + j - 1 of
+ *   snapshots  [num_snapshots, H, d_v, d_k] fp32,
+ * where base_n = sum over m < n of floor(L_m / snapshot_every): the snapshots
+ * of all sequences in sequence order, each sequence's in token order.  When
+ * snapshot_every divides L_n, the last one equals that sequence's final state.
+ *
+ *   snapshot_every  > 0 (else KDA_ERR_SHAPE); this build supports multiples of
+ *                   32 only (else KDA_ERR_UNSUPPORTED).
+ *   num_snapshots   entries the buffer holds (>= 0).  Dense: must be at least
+ *                   batch * floor(seq_len / snapshot_every) (else
+ *                   KDA_ERR_SHAPE).  Packed: the host cannot read cu_seqlens,
+ *                   so the count is not checked; entries at or beyond
+ *                   num_snapshots are not written.
+ *   snapshots       caller-owned device buffer, 16-byte aligned; may be NULL
+ *                   only when num_snapshots == 0.  It must not overlap any
+ *                   input, out or final_state (KDA_ERR_ALIAS).  Entries no
+ *                   sequence reaches are left untouched.
+ *
+ * Returns KDA_OK or a kda_status error code.
+ */
+int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, const float *initial_state,
+                            const int32_t *cu_seqlens, void *out, float *final_state,
+                            float *snapshots, int32_t snapshot_every, int32_t num_snapshots,
+                            int32_t batch, int32_t seq_len, int32_t num_heads,
+                            int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs,
+                            int32_t dtype, hipStream_t stream);
 
 /*
  * kda_decode_step -- one new token per session against a stored state: the

@@ -7,6 +7,8 @@ the HIP library (``gated_delta_rule_81_amd``) and neither imports the other.
 Contents
   * ``kda_forward`` -- ctypes front end of ``kda_oracle.c``: the token-by-token
     recurrence in fp64 (the definition the GPU path must reproduce).
+  * ``kda_snapshots`` -- the same recurrence with the state recorded after
+    every N tokens of each sequence.
   * ``forms.projection_forward`` -- a second fp64 witness that builds the
     explicit d_k x d_k transition matrices of the printed KDA update.
   * ``forms.brute_force_exact`` -- exact-rational evaluation through transition
@@ -136,6 +138,53 @@ def kda_forward_dense(q, k, v, log_alpha, beta, state0=None, threads: int = 0):
         _f64(beta).reshape(B * T, H), state0,
         seq_start=np.arange(B + 1, dtype=np.int64) * T, threads=threads)
     return out.reshape(B, T, H, dv), sT
+
+
+def kda_snapshots(q, k, v, log_alpha, beta, every: int, state0=None, seq_start=None,
+                  threads: int = 0):
+    """The recurrence with its state recorded after every ``every`` tokens of
+    each sequence: restartable checkpoints ([K3-memory] §5).
+
+    The definition written out: the state S after the first j * every tokens of
+    sequence n, j = 1 .. floor(L_n / every).  It is computed by running the
+    token recurrence one segment of ``every`` tokens at a time, each segment
+    starting from the state the previous one ended in (all sequences' j-th
+    segments in one ``kda_forward`` call).  Same arguments as ``kda_forward``.
+    Returns (out [T, H, d_v], final state [N, H, d_v, d_k], snapshots
+    [S, H, d_v, d_k]) with S = sum_n floor(L_n / every), sequences in order and
+    each sequence's snapshots in token order.
+    """
+    every = int(every)
+    if every <= 0:
+        raise ValueError("every must be positive")
+    q = _f64(q)
+    T, H, dk = q.shape
+    k, v, log_alpha, beta = _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    dv = v.shape[2]
+    if seq_start is None:
+        seq_start = [0, T]
+    starts = np.asarray(seq_start, dtype=np.int64)
+    N = starts.shape[0] - 1
+    lengths = starts[1:] - starts[:-1]
+    counts = lengths // every
+    base = np.concatenate([[0], np.cumsum(counts)])
+    snaps = np.zeros((int(base[-1]), H, dv, dk), dtype=np.float64)
+    out = np.zeros((T, H, dv), dtype=np.float64)
+    state = (np.zeros((N, H, dv, dk)) if state0 is None else _f64(state0, (N, H, dv, dk)).copy())
+    nseg = int(np.max((lengths + every - 1) // every)) if N > 0 else 0
+    for j in range(nseg):
+        # segment j of every sequence: tokens [start + j*every, min(start + (j+1)*every, end))
+        lo = np.minimum(starts[:-1] + j * every, starts[1:])
+        hi = np.minimum(starts[:-1] + (j + 1) * every, starts[1:])
+        idx = np.concatenate([np.arange(a, b) for a, b in zip(lo, hi)]).astype(np.int64)
+        seg_start = np.concatenate([[0], np.cumsum(hi - lo)])
+        o, state = kda_forward(q[idx], k[idx], v[idx], log_alpha[idx], beta[idx], state,
+                               seq_start=seg_start, threads=threads)
+        out[idx] = o
+        for n in range(N):
+            if j < counts[n]:
+                snaps[base[n] + j] = state[n]
+    return out, state, snaps
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, state, threads: int = 0):

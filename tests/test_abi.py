@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["kda_abi_version", "kda_chunk_fwd", "kda_decode_step", "kda_status_string"])
+        ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step",
+         "kda_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
     for code in range(-7, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
@@ -161,6 +162,69 @@ def test_chunk_zero_tokens_allows_null_inputs():
     # T = 0 still copies initial -> final state, so it reaches the device check
     rc = call_chunk(seq_len=0, q=None, k=None, v=None, log_alpha=None, beta=None, out=None)
     assert rc in (DEVICE, OK)
+
+
+# ---------------------------------------------------------------- chunk_fwd_snapshots
+def call_snap(snapshots="auto", snapshot_every=64, num_snapshots=None, **kw):
+    a = chunk_args(**kw)
+    if snapshots == "auto":
+        snapshots = (1 << 50)
+    if num_snapshots is None:
+        num_snapshots = a["batch"] * (a["seq_len"] // snapshot_every) if snapshot_every > 0 else 1
+    return _lib.lib().kda_chunk_fwd_snapshots(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"],
+        a["cu_seqlens"], a["out"], a["final_state"], snapshots, snapshot_every, num_snapshots,
+        a["batch"], a["seq_len"], a["num_heads"], a["head_dim_k"], a["head_dim_v"],
+        a["num_seqs"], a["dtype"], a["stream"])
+
+
+def test_snapshots_valid_call_reaches_the_device_check():
+    assert call_snap() in (DEVICE, OK)
+    assert call_snap(snapshot_every=32, seq_len=100) in (DEVICE, OK)
+
+
+@pytest.mark.parametrize("every", [0, -32])
+def test_snapshots_interval_must_be_positive(every):
+    assert call_snap(snapshot_every=every, num_snapshots=1) == SHAPE
+
+
+@pytest.mark.parametrize("every", [1, 48, 100])
+def test_snapshots_interval_must_be_a_chunk_multiple(every):
+    assert call_snap(snapshot_every=every) == UNSUP
+
+
+def test_snapshots_dense_capacity_is_checked():
+    # batch 2 x floor(200 / 64) = 6 entries needed
+    assert call_snap(seq_len=200, num_snapshots=5) == SHAPE
+    assert call_snap(seq_len=200, num_snapshots=6) in (DEVICE, OK)
+    assert call_snap(seq_len=200, num_snapshots=-1) == SHAPE
+    # fewer tokens than one interval: no entry needed, the buffer may be NULL
+    assert call_snap(seq_len=63, snapshots=None, num_snapshots=0) in (DEVICE, OK)
+
+
+def test_snapshots_packed_capacity_is_not_checked_on_host():
+    b = Buf()
+    assert call_snap(cu_seqlens=b(), batch=1, num_seqs=3, seq_len=500,
+                     num_snapshots=1) in (DEVICE, OK)
+
+
+def test_snapshots_null_buffer_with_entries():
+    assert call_snap(snapshots=None, num_snapshots=6, seq_len=200) == NULL
+
+
+def test_snapshots_misaligned_and_aliased():
+    a = chunk_args()
+    assert call_snap(snapshots=(1 << 50) + 8) == ALIGN
+    assert call_snap(snapshots=a["out"]) == ALIAS
+    assert call_snap(snapshots=a["final_state"] + 1024) == ALIAS
+    assert call_snap(snapshots=a["q"]) == ALIAS
+    assert call_snap(snapshots=a["initial_state"]) == ALIAS
+
+
+def test_snapshots_share_the_chunk_fwd_checks():
+    assert call_snap(q=None) == NULL
+    assert call_snap(dtype=F32) == UNSUP
+    assert call_snap(batch=0) == OK
 
 
 # ---------------------------------------------------------------- decode_step

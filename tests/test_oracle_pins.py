@@ -315,3 +315,63 @@ def test_rejects_bad_sequence_offsets():
         oracle.kda_forward(q, k, v, g, b, seq_start=[0, 6, 4, 10])
     with pytest.raises(ValueError):
         oracle.kda_forward(q, k, v, g, b, seq_start=[0, 11])
+
+
+# ---------------------------------------------------------------- state snapshots
+# [K3-memory] §5: the recurrent state kept every N tokens as a restartable
+# checkpoint.  Definition: the state after the first j * N tokens of a sequence.
+SNAP_LENS = [0, 5, 16, 33, 70, 96]
+
+
+def _snap_case(seed, H=2, dk=6, dv=5):
+    rng = np.random.default_rng(seed)
+    T = sum(SNAP_LENS)
+    q, k, v, g, beta = _rand_case(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((len(SNAP_LENS), H, dv, dk)) * 0.1
+    starts = np.concatenate([[0], np.cumsum(SNAP_LENS)]).astype(np.int64)
+    return q, k, v, beta, g, s0, starts
+
+
+@pytest.mark.parametrize("every", [1, 16, 32])
+def test_snapshots_are_the_prefix_states(every):
+    q, k, v, beta, g, s0, starts = _snap_case(7)
+    out, fin, snaps = oracle.kda_snapshots(q, k, v, g, beta, every, state0=s0, seq_start=starts)
+    counts = [n // every for n in SNAP_LENS]
+    assert snaps.shape[0] == sum(counts)
+    i = 0
+    for n, cnt in enumerate(counts):
+        a = starts[n]
+        for j in range(1, cnt + 1):
+            sl = slice(a, a + j * every)
+            _, ref = oracle.kda_forward(q[sl], k[sl], v[sl], g[sl], beta[sl], state0=s0[n:n + 1])
+            assert _rel(snaps[i], ref[0]) < 1e-13
+            i += 1
+    # outputs and final states are those of the uninterrupted recurrence
+    out_ref, fin_ref = oracle.kda_forward(q, k, v, g, beta, state0=s0, seq_start=starts)
+    assert _rel(out, out_ref) < 1e-13 and _rel(fin, fin_ref) < 1e-13
+
+
+def test_snapshots_beta_zero_closed_form():
+    """beta = 0: snapshot j is the initial state decayed per channel over the
+    first j * N tokens, M[v, c] * exp(sum of log_alpha[:, c])."""
+    q, k, v, beta, g, s0, starts = _snap_case(8)
+    every = 16
+    _, _, snaps = oracle.kda_snapshots(q, k, v, g, np.zeros_like(beta), every, state0=s0,
+                                       seq_start=starts)
+    i = 0
+    for n, L in enumerate(SNAP_LENS):
+        for j in range(1, L // every + 1):
+            a = starts[n]
+            decay = np.exp(g[a:a + j * every].sum(axis=0))  # [H, d_k]
+            ref = s0[n] * decay[:, None, :]
+            assert _rel(snaps[i], ref) < 1e-13
+            i += 1
+    assert i == snaps.shape[0]
+
+
+def test_last_snapshot_is_the_final_state_when_the_interval_divides_the_length():
+    q, k, v, beta, g, s0, starts = _snap_case(9)
+    _, fin, snaps = oracle.kda_snapshots(q, k, v, g, beta, 16, state0=s0, seq_start=starts)
+    # lengths 16 and 96 are multiples of 16: their last snapshots are entries 0 and -1
+    assert np.array_equal(snaps[0], fin[2])
+    assert np.array_equal(snaps[-1], fin[5])
