@@ -49,18 +49,20 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def prefill_bytes(T_tokens, H, d, n_seqs, esz=2):
+def prefill_bytes(T_tokens, H, d, n_seqs, esz=2, gate_width=None):
     """Algorithmic HBM bytes of one kda_chunk_fwd: read q, k, v (esz each),
-    log_alpha (fp32), beta (fp32), the initial state; write out (esz) and the
-    final state."""
-    per_token_head = 3 * d * esz + 4 * d + 4 + d * esz
+    log_alpha (fp32, gate_width per token-head: d, or 1 for a scalar gate),
+    beta (fp32), the initial state; write out (esz) and the final state."""
+    gw = d if gate_width is None else gate_width
+    per_token_head = 3 * d * esz + 4 * gw + 4 + d * esz
     return T_tokens * H * per_token_head + 2 * n_seqs * H * d * d * 4
 
 
-def decode_bytes(B, H, d, esz=2):
+def decode_bytes(B, H, d, esz=2, gate_width=None):
     """Algorithmic HBM bytes of one kda_decode_step: the fp32 state read and
-    written once, plus q, k, v, log_alpha, beta in and out."""
-    return B * H * (2 * d * d * 4 + 3 * d * esz + 4 * d + 4 + d * esz)
+    written once, plus q, k, v, log_alpha (gate_width per unit), beta in and out."""
+    gw = d if gate_width is None else gate_width
+    return B * H * (2 * d * d * 4 + 3 * d * esz + 4 * gw + 4 + d * esz)
 
 
 def source_digest():
@@ -102,8 +104,9 @@ def cpu_baseline(inp, heads, threads):
     b = inp["beta"][0, :, :heads].numpy().astype(np.float64)
     s0 = inp["initial_state"][:, :heads].numpy().astype(np.float64)
     T = q.shape[0]
+    run = oracle.gdn_forward if g.ndim == 2 else oracle.kda_forward  # scalar or channel gates
     t0 = time.perf_counter()
-    oracle.kda_forward(q, k, v, g, b, state0=s0, threads=threads)
+    run(q, k, v, g, b, state0=s0, threads=threads)
     dt = time.perf_counter() - t0
     return {"value": T * heads / dt / H, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
@@ -121,10 +124,15 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="time kda_chunk_fwd only (for counter passes); no decode fields")
+    ap.add_argument("--scalar-gate", action="store_true",
+                    help="time the scalar-gate (Gated DeltaNet) entry points, one gate per "
+                         "token and head (the first channel of the seeded gates)")
     ap.add_argument("--snapshot-every", type=int, default=0,
                     help="time kda_chunk_fwd_snapshots with a state snapshot every N tokens "
                          "(a multiple of 32) instead of kda_chunk_fwd")
     args = ap.parse_args()
+    if args.scalar_gate and args.snapshot_every:
+        ap.error("--scalar-gate and --snapshot-every time different entry points; pick one")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
               "(run with --gpus 1)", file=sys.stderr)
@@ -146,6 +154,10 @@ def main():
         w_dec = synth.replace(w_dec, batch=1, heads=1, steps=1)
     log("generating", w_dec.notes)
     dec = synth.decode_inputs(w_dec)
+    sg = args.scalar_gate
+    if sg:  # one gate per (token, head): the first channel of the seeded gates
+        pre["log_alpha"] = pre["log_alpha"][..., 0].contiguous()
+        dec["log_alpha"] = dec["log_alpha"][..., 0].contiguous()
     P = {key: pre[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta", "initial_state")}
     Dn = {key: dec[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
     state = dec["state"].to(dev)
@@ -166,13 +178,13 @@ def main():
                                     snapshots=snaps)
         else:
             kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"],
-                          P["initial_state"], out=out, final_state=fin)
+                          P["initial_state"], out=out, final_state=fin, scalar_gate=sg)
 
     def step(s):
         prefill()
         t = s % w_dec.steps
         kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
-                        state, out=dout)
+                        state, out=dout, scalar_gate=sg)
 
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
@@ -192,7 +204,7 @@ def main():
         e[1].record(stream)
         t = (args.warmup + s) % w_dec.steps
         kda.decode_step(Dn["q"][t], Dn["k"][t], Dn["v"][t], Dn["log_alpha"][t], Dn["beta"][t],
-                        state, out=dout)
+                        state, out=dout, scalar_gate=sg)
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -213,13 +225,14 @@ def main():
         log("copy calibration: 3 x 1 GiB device-to-device copies")
 
     T_tok = w_pre.batch * w_pre.seq_len
-    pbytes = prefill_bytes(T_tok, w_pre.heads, w_pre.head_dim, w_pre.batch)
+    gw = 1 if sg else None
+    pbytes = prefill_bytes(T_tok, w_pre.heads, w_pre.head_dim, w_pre.batch, gate_width=gw)
     pbytes += n_snap * w_pre.heads * w_pre.head_dim * w_pre.head_dim * 4  # snapshot writes
-    dbytes = decode_bytes(w_dec.batch, w_dec.heads, w_dec.head_dim)
+    dbytes = decode_bytes(w_dec.batch, w_dec.heads, w_dec.head_dim, gate_width=gw)
     pre_gbs = pbytes / (pre_avg * 1e-3) / 1e9
     dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
-    traffic = measured_traffic() if every == 0 else None
+    traffic = measured_traffic() if every == 0 and not sg else None
 
     result = {
         "metric": "KDA chunked-fwd tokens/s (H=96,d=128,T=32K); decode state-update HBM GB/s",
@@ -234,10 +247,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": ("kda_chunk_fwd" if every == 0 else
+        "config": {"workload": ("kda_chunk_fwd_scalar_gate" if sg else "kda_chunk_fwd"
+                                if every == 0 else
                                 f"kda_chunk_fwd_snapshots (every {every} tokens)")
                                + " B=1 H=96 T=32768 d_k=d_v=128 bf16 q/k/v, "
-                               "fp32 gates/state, chunk 32 + kda_decode_step B=256 H=96 d=128",
+                               "fp32 gates/state, chunk 32 + "
+                               + ("kda_decode_step_scalar_gate" if sg else "kda_decode_step")
+                               + " B=256 H=96 d=128",
+                   "scalar_gate": sg,
                    "snapshot_every": every or None,
                    "prefill_tokens": T_tok, "heads": w_pre.heads, "head_dim": w_pre.head_dim,
                    "decode_sessions": w_dec.batch},

@@ -27,6 +27,10 @@ SIGNATURES = {
     "kda_chunk_fwd_snapshots": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp, _fp,
                                  _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _vp], ctypes.c_int),
+    "kda_chunk_fwd_scalar_gate": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp,
+                                   _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "kda_decode_step_scalar_gate": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,
+                                     _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "kda_decode_step": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,
                          _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "kda_status_string": ([ctypes.c_int], ctypes.c_char_p),

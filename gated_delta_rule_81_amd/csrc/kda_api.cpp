@@ -71,14 +71,15 @@ const char *kda_status_string(int status) {
 
 namespace {
 
-// Shared by kda_chunk_fwd and kda_chunk_fwd_snapshots (snapshots == NULL and
-// num_snapshots == 0 for the former).
+// Shared by the prefill entry points: kda_chunk_fwd (no snapshots, gates per
+// channel), kda_chunk_fwd_snapshots and kda_chunk_fwd_scalar_gate (log_alpha
+// [T, H]: one gate per token and head).
 int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log_alpha,
                    const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                    void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                    int32_t num_snapshots, int32_t batch, int32_t seq_len, int32_t num_heads,
                    int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs, int32_t dtype,
-                   hipStream_t stream) {
+                   bool scalar_gate, hipStream_t stream) {
     // sizes
     if (batch < 0 || seq_len < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0)
         return KDA_ERR_SHAPE;
@@ -109,14 +110,16 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
     // the kernel addresses 64 tokens of one tensor with 32-bit byte offsets
     if ((int64_t)num_heads * d * 4 * 64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     // alignment
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
-        !aligned4(beta) || !aligned16(initial_state) || !aligned16(out) ||
-        !aligned16(final_state) || !aligned4(cu_seqlens) || !aligned16(snapshots))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !(scalar_gate ? aligned4(log_alpha) : aligned16(log_alpha)) || !aligned4(beta) ||
+        !aligned16(initial_state) || !aligned16(out) || !aligned16(final_state) ||
+        !aligned4(cu_seqlens) || !aligned16(snapshots))
         return KDA_ERR_ALIGN;
     // aliasing
     const uint64_t state_bytes = (uint64_t)nseq * num_heads * d * d * 4;
     const Range rq{q, th * d * esz}, rk{k, th * d * esz}, rv{v, th * d * esz},
-        rg{log_alpha, th * d * 4}, rb{beta, th * 4}, rs0{initial_state, state_bytes},
+        rg{log_alpha, th * (scalar_gate ? 1 : d) * 4}, rb{beta, th * 4},
+        rs0{initial_state, state_bytes},
         rcu{cu_seqlens, packed ? (uint64_t)(nseq + 1) * 4 : 0}, ro{out, th * d * esz},
         rs1{final_state, state_bytes},
         rsn{snapshots, (uint64_t)num_snapshots * num_heads * d * d * 4};
@@ -135,7 +138,42 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
     const int rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                          final_state, num_snapshots > 0 ? snapshots : nullptr,
                                          snapshot_every, num_snapshots, (int32_t)nseq, seq_len,
-                                         (int32_t)tokens, num_heads, d, dtype, stream);
+                                         (int32_t)tokens, num_heads, d, dtype, scalar_gate ? 1 : 0,
+                                         stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// Shared by kda_decode_step and kda_decode_step_scalar_gate (log_alpha [B, H]).
+int decode_impl(const void *q, const void *k, const void *v, const float *log_alpha,
+                const float *beta, float *state, void *out, int32_t batch, int32_t num_heads,
+                int32_t head_dim_k, int32_t head_dim_v, int32_t dtype, bool scalar_gate,
+                hipStream_t stream) {
+    if (batch < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0) return KDA_ERR_SHAPE;
+    if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
+    const uint64_t units = (uint64_t)batch * num_heads;
+    if (units > 0 && (!q || !k || !v || !log_alpha || !beta || !state || !out))
+        return KDA_ERR_NULL;
+    if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
+    const int d = head_dim_k;
+    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !(scalar_gate ? aligned4(log_alpha) : aligned16(log_alpha)) || !aligned4(beta) ||
+        !aligned16(state) || !aligned16(out))
+        return KDA_ERR_ALIGN;
+    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
+    const Range ro{out, units * d * esz};
+    const Range others[] = {{q, units * d * esz}, {k, units * d * esz}, {v, units * d * esz},
+                            {log_alpha, units * (scalar_gate ? 1 : d) * 4}, {beta, units * 4},
+                            {state, units * d * d * 4}};
+    for (const Range &r : others)
+        if (overlap(ro, r)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 5; ++i)
+        if (overlap(others[5], others[i])) return KDA_ERR_ALIAS;
+    if (units == 0) return KDA_OK;
+    const int st = check_device();
+    if (st != KDA_OK) return st;
+    const int rc = kda::launch_decode_step(q, k, v, log_alpha, beta, state, out, (int64_t)units,
+                                           d, dtype, scalar_gate ? 1 : 0, stream);
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -150,7 +188,18 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_
                   int32_t dtype, hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state,
                           nullptr, 0, 0, batch, seq_len, num_heads, head_dim_k, head_dim_v,
-                          num_seqs, dtype, stream);
+                          num_seqs, dtype, false, stream);
+}
+
+int kda_chunk_fwd_scalar_gate(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *beta,
+                              const float *initial_state, const int32_t *cu_seqlens, void *out,
+                              float *final_state, int32_t batch, int32_t seq_len,
+                              int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                              int32_t num_seqs, int32_t dtype, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state,
+                          nullptr, 0, 0, batch, seq_len, num_heads, head_dim_k, head_dim_v,
+                          num_seqs, dtype, true, stream);
 }
 
 int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const float *log_alpha,
@@ -163,38 +212,22 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
     if (snapshot_every <= 0) return KDA_ERR_SHAPE;
     return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state,
                           snapshots, snapshot_every, num_snapshots, batch, seq_len, num_heads,
-                          head_dim_k, head_dim_v, num_seqs, dtype, stream);
+                          head_dim_k, head_dim_v, num_seqs, dtype, false, stream);
 }
 
 int kda_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                     const float *beta, float *state, void *out, int32_t batch, int32_t num_heads,
                     int32_t head_dim_k, int32_t head_dim_v, int32_t dtype, hipStream_t stream) {
-    if (batch < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0) return KDA_ERR_SHAPE;
-    if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
-    const uint64_t units = (uint64_t)batch * num_heads;
-    if (units > 0 && (!q || !k || !v || !log_alpha || !beta || !state || !out))
-        return KDA_ERR_NULL;
-    if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
-    const int d = head_dim_k;
-    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
-        !aligned4(beta) || !aligned16(state) || !aligned16(out))
-        return KDA_ERR_ALIGN;
-    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
-    const Range ro{out, units * d * esz};
-    const Range others[] = {{q, units * d * esz}, {k, units * d * esz}, {v, units * d * esz},
-                            {log_alpha, units * d * 4}, {beta, units * 4},
-                            {state, units * d * d * 4}};
-    for (const Range &r : others)
-        if (overlap(ro, r)) return KDA_ERR_ALIAS;
-    for (int i = 0; i < 5; ++i)
-        if (overlap(others[5], others[i])) return KDA_ERR_ALIAS;
-    if (units == 0) return KDA_OK;
-    const int st = check_device();
-    if (st != KDA_OK) return st;
-    const int rc = kda::launch_decode_step(q, k, v, log_alpha, beta, state, out, (int64_t)units,
-                                           d, dtype, stream);
-    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+    return decode_impl(q, k, v, log_alpha, beta, state, out, batch, num_heads, head_dim_k,
+                       head_dim_v, dtype, false, stream);
+}
+
+int kda_decode_step_scalar_gate(const void *q, const void *k, const void *v,
+                                const float *log_alpha, const float *beta, float *state,
+                                void *out, int32_t batch, int32_t num_heads, int32_t head_dim_k,
+                                int32_t head_dim_v, int32_t dtype, hipStream_t stream) {
+    return decode_impl(q, k, v, log_alpha, beta, state, out, batch, num_heads, head_dim_k,
+                       head_dim_v, dtype, true, stream);
 }
 
 }  // extern "C"

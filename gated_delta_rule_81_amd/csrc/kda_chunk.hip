@@ -83,7 +83,7 @@ __device__ __forceinline__ int phys(int i) {
     }
 }
 
-template <typename T, int D, int DVS>
+template <typename T, int D, int DVS, bool SG>
 struct Cfg {
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int kPad = 16 / SZ;
@@ -101,13 +101,15 @@ struct Cfg {
     static constexpr int VTH = kC * DVS / VE;  // preparation threads that move the V slice
     static constexpr int RW = 4 * SZ / 4;    // words per 4-channel run of k / q
     // whole-row loads: 16 bytes per lane, a row of k / q (RBK bytes), log_alpha
-    // (RBG) or the V slice (RBV) covered by RBX / 16 consecutive lanes
-    static constexpr int RBK = D * SZ, RBG = D * 4, RBV = DVS * SZ;
+    // (RBG; none with a scalar gate, which is loaded like beta) or the V slice
+    // (RBV) covered by RBX / 16 consecutive lanes
+    static constexpr int RBK = D * SZ, RBG = SG ? 0 : D * 4, RBV = DVS * SZ;
     static constexpr int IK = RBK / 16 / 2 / PW;  // k (and q) load instructions per wave
     static constexpr int IG = RBG / 16 / 2 / PW;  // log_alpha load instructions per wave
     static constexpr int NIV = RBV / 16 / 2;      // V load instructions (waves 0 .. NIV-1)
     static constexpr int IO = RBV / 16 / 2 / SWV; // O store instructions per scan wave
     static constexpr int LSK = RBK + 16, LSG = RBG + 16, LSV = RBV + 16;  // staging row bytes
+    static constexpr int NGA = IG > 0 ? IG : 1;   // register slots for the gate pieces
 
     // one buffer set of prepared operands (byte offsets inside the set)
     static constexpr int B_TK = kC * LDK * SZ;
@@ -122,7 +124,8 @@ struct Cfg {
                          oAt = oKM + B_TK;
     // staging of the next chunk's raw rows (k, q, log_alpha, V slice, beta)
     static constexpr int oRK = oAt + 2 * kBS * LDAT * 4, oRQ = oRK + kC * LSK,
-                         oRG = oRQ + kC * LSK, oRV = oRG + kC * LSG, oRB = oRV + kC * LSV;
+                         oRG = oRQ + kC * LSK, oRV = oRG + (SG ? kC * 4 : kC * LSG),
+                         oRB = oRV + kC * LSV;
     // O staging (all scan waves), stored as whole rows in the next phase
     static constexpr int oO = oRB + kC * 4, BYTES = oO + kC * LSV;
 
@@ -130,7 +133,7 @@ struct Cfg {
     static_assert(DVS % 16 == 0 && D % DVS == 0, "d_v slice");
     static_assert(VTH <= PW * 64 && VTH >= kC, "V slice map");
     static_assert(D % KB == 0, "state contraction blocks");
-    static_assert(IK >= 1 && IG >= 1 && IO >= 1 && NIV <= PW &&
+    static_assert(IK >= 1 && (IG >= 1 || SG) && IO >= 1 && NIV <= PW &&
                       IK * PW * 2 * 16 == RBK && IG * PW * 2 * 16 == RBG &&
                       IO * SWV * 2 * 16 == RBV, "whole-row load maps");
     static_assert(SET % 16 == 0 && oKM % 16 == 0 && oAt % 16 == 0 && oO % 16 == 0 &&
@@ -152,7 +155,8 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 template <typename T>
 __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v,
                                               const float *log_alpha, const float *beta,
-                                              int64_t tok0, int nvalid, int H, int D) {
+                                              int64_t tok0, int nvalid, int H, int D,
+                                              bool scalar_gate) {
     const int64_t e0 = tok0 * H * D;
     const int elems = nvalid * H * D;  // the host keeps 64 * H * D * 4 < 2^31
     ChunkSrc s;
@@ -162,7 +166,10 @@ __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v
                                             kRsrcWord3);
     s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, elems * (int)sizeof(T),
                                             kRsrcWord3);
-    s.g = __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, elems * 4, kRsrcWord3);
+    s.g = scalar_gate ? __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + tok0 * H), 0,
+                                                          nvalid * H * 4, kRsrcWord3)
+                      : __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, elems * 4,
+                                                          kRsrcWord3);
     s.b = __builtin_amdgcn_make_buffer_rsrc((void *)(beta + tok0 * H), 0, nvalid * H * 4,
                                             kRsrcWord3);
     return s;
@@ -236,21 +243,22 @@ __device__ __forceinline__ void st4(float *p, const float (&f)[4]) {
 // each of k and q, IG of log_alpha, one of the V slice (last NIV waves), one
 // beta (last wave).  Waves 0 and 1 run the triangular solves, so the extra
 // pieces go to the other waves.
-template <typename T, int D, int DVS>
+template <typename T, int D, int DVS, bool SG>
 struct ChunkRegs {
-    typedef Cfg<T, D, DVS> G;
-    Raw<4> k[G::IK], q[G::IK], g[G::IG], v;
-    float beta;
+    typedef Cfg<T, D, DVS, SG> G;
+    Raw<4> k[G::IK], q[G::IK], g[G::NGA], v;
+    float beta, gs;  // gs: the scalar gate (scalar-gate variant only)
 };
 
 // Where a preparation thread's pieces come from (byte offsets relative to a
 // chunk's first token; loop-invariant) and where they go in the staging area.
-template <typename T, int D, int DVS>
+template <typename T, int D, int DVS, bool SG>
 struct ChunkOffsets {
-    typedef Cfg<T, D, DVS> G;
-    int gk[G::IK], sk[G::IK], gg[G::IG], sg[G::IG], gv, sv, gb;
+    typedef Cfg<T, D, DVS, SG> G;
+    int gk[G::IK], sk[G::IK], gg[G::NGA], sg[G::NGA], gv, sv, gb;
     __device__ ChunkOffsets(int wave, int lane, int h, int H, int v0) {
-        constexpr int LK = G::RBK / 16, LG = G::RBG / 16, LV = G::RBV / 16;
+        constexpr int LK = G::RBK / 16, LG = G::RBG / 16 > 0 ? G::RBG / 16 : 1,
+                      LV = G::RBV / 16;
 #pragma unroll
         for (int i = 0; i < G::IK; ++i) {
             const int p = (wave * G::IK + i) * 64 + lane, row = p / LK, b = 16 * (p % LK);
@@ -270,11 +278,11 @@ struct ChunkOffsets {
     }
 };
 
-template <typename T, int D, int DVS>
-__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS> &R, const ChunkSrc &s,
-                                           const ChunkOffsets<T, D, DVS> &o, int wave,
+template <typename T, int D, int DVS, bool SG>
+__device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS, SG> &R, const ChunkSrc &s,
+                                           const ChunkOffsets<T, D, DVS, SG> &o, int wave,
                                            int lane) {
-    typedef Cfg<T, D, DVS> G;
+    typedef Cfg<T, D, DVS, SG> G;
 #pragma unroll
     for (int i = 0; i < G::IK; ++i) {
         R.k[i] = buf_load<4>(s.k, o.gk[i]);
@@ -283,15 +291,18 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS> &R, const ChunkS
 #pragma unroll
     for (int i = 0; i < G::IG; ++i) R.g[i] = buf_load<4>(s.g, o.gg[i]);
     if (wave >= G::PW - G::NIV) R.v = buf_load<4>(s.v, o.gv);
-    if (wave == G::PW - 1 && lane < kC) R.beta = __uint_as_float(buf_load<1>(s.b, o.gb).w[0]);
+    if (wave == G::PW - 1 && lane < kC) {
+        R.beta = __uint_as_float(buf_load<1>(s.b, o.gb).w[0]);
+        if constexpr (SG) R.gs = __uint_as_float(buf_load<1>(s.g, o.gb).w[0]);
+    }
 }
 
 // The pieces into the staging area (waits for the loads to land).
-template <typename T, int D, int DVS>
-__device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS> &R, unsigned char *smem,
-                                            const ChunkOffsets<T, D, DVS> &o, int wave,
+template <typename T, int D, int DVS, bool SG>
+__device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS, SG> &R, unsigned char *smem,
+                                            const ChunkOffsets<T, D, DVS, SG> &o, int wave,
                                             int lane) {
-    typedef Cfg<T, D, DVS> G;
+    typedef Cfg<T, D, DVS, SG> G;
     auto st16 = [](unsigned char *p, const Raw<4> &x) {
         *reinterpret_cast<u32x4 *>(p) = u32x4{x.w[0], x.w[1], x.w[2], x.w[3]};
     };
@@ -303,7 +314,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS> &R, unsig
 #pragma unroll
     for (int i = 0; i < G::IG; ++i) st16(smem + G::oRG + o.sg[i], R.g[i]);
     if (wave >= G::PW - G::NIV) st16(smem + G::oRV + o.sv, R.v);
-    if (wave == G::PW - 1 && lane < kC) reinterpret_cast<float *>(smem + G::oRB)[lane] = R.beta;
+    if (wave == G::PW - 1 && lane < kC) {
+        reinterpret_cast<float *>(smem + G::oRB)[lane] = R.beta;
+        if constexpr (SG) reinterpret_cast<float *>(smem + G::oRG)[lane] = R.gs;
+    }
 }
 
 // DPP helpers (all lanes active).
@@ -378,7 +392,7 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
     return acc;
 }
 
-template <typename T, int D, int DVS>
+template <typename T, int D, int DVS, bool SG>
 __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -386,7 +400,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     T *__restrict__ out, float *__restrict__ final_state, float *__restrict__ snapshots,
     int snap_every, int snap_cap, int num_seqs, int seq_len, int total_tokens, int H, int units,
     int units_per_xcd) {
-    typedef Cfg<T, D, DVS> G;
+    typedef Cfg<T, D, DVS, SG> G;
     typedef Mma<T> M;
     typedef ScanMma<T> SM;
     constexpr int NS = D / DVS;
@@ -445,11 +459,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         const int r = lane & 15;
         const int c = 4 * (4 * wave + (lane >> 4));
         const int pc = phys<T>(c);
-        const ChunkOffsets<T, D, DVS> offs(wave, lane, h, H, v0);
-        ChunkRegs<T, D, DVS> R;
+        const ChunkOffsets<T, D, DVS, SG> offs(wave, lane, h, H, v0);
+        ChunkRegs<T, D, DVS, SG> R;
         if (nchunks > 0) {
             load_chunk(R, chunk_src(q, k, v, log_alpha, beta, tbeg,
-                                    (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D),
+                                    (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D, SG),
                        offs, wave, lane);
             stage_chunk(R, smem, offs, wave, lane);
         }
@@ -476,12 +490,12 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     const int64_t ntok0 = tbeg + (int64_t)(tick + 1) * kC;
                     load_chunk(R, chunk_src(q, k, v, log_alpha, beta, ntok0,
                                             (int)((tend - ntok0) < kC ? (tend - ntok0) : kC), H,
-                                            D),
+                                            D, SG),
                                offs, wave, lane);
                 }
                 // this chunk's rows r and r + 16 from the staging area
                 Raw<G::RW> rk[2], rq[2];
-                Raw<4> rg[2];
+                float d0[4], d1[4], erho[4];  // gates of rows r, r + 16 (channels c .. c + 3)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int row = r + kBS * j;
@@ -500,16 +514,35 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) { rk[j].w[i] = a[i]; rq[j].w[i] = b[i]; }
                     }
-                    const u32x4 gg = *reinterpret_cast<const u32x4 *>(
-                        smem + G::oRG + row * G::LSG + c * 4);
+                    if constexpr (!SG) {
+                        const f32x4 gg = *reinterpret_cast<const f32x4 *>(
+                            smem + G::oRG + row * G::LSG + c * 4);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) rg[j].w[i] = gg[i];
+                        for (int i = 0; i < 4; ++i) (j ? d1 : d0)[i] = gg[i];
+                    }
                 }
                 // block-relative inclusive prefix of the log2-gates (block 0's is
                 // chunk-relative); rho = Gamma_15 = block 0's total (lane 15)
-                float d0[4], d1[4], erho[4];
-                unpack<float, 4>(rg[0], d0);
-                unpack<float, 4>(rg[1], d1);
+                if constexpr (SG) {
+                    // one gate per token: a single prefix serves all four channels
+                    const float *gsv = reinterpret_cast<const float *>(smem + G::oRG);
+                    float x = gsv[r] * kLog2e, y = gsv[r + kBS] * kLog2e;
+                    x += dpp_row_shr<1>(x);
+                    y += dpp_row_shr<1>(y);
+                    x += dpp_row_shr<2>(x);
+                    y += dpp_row_shr<2>(y);
+                    x += dpp_row_shr<4>(x);
+                    y += dpp_row_shr<4>(y);
+                    x += dpp_row_shr<8>(x);
+                    y += dpp_row_shr<8>(y);
+                    const float er = fast_exp2(dpp<0x15f, 0xf>(x));  // row_newbcast:15
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        d0[e] = x;
+                        d1[e] = y;
+                        erho[e] = er;
+                    }
+                } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float x = d0[e] * kLog2e, y = d1[e] * kLog2e;
@@ -524,6 +557,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     d0[e] = x;
                     d1[e] = y;
                     erho[e] = fast_exp2(dpp<0x15f, 0xf>(x));  // row_newbcast:15
+                }
                 }
                 float kf[4], qf[4];
                 float kt0[4], kt1[4], ep1[4];
@@ -860,7 +894,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     }
 }
 
-template <typename T, int D, int DVS>
+template <typename T, int D, int DVS, bool SG>
 int launch(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
            const float *initial_state, const int32_t *cu_seqlens, void *out, float *final_state,
            float *snapshots, int snap_every, int snap_cap, int num_seqs, int seq_len,
@@ -870,12 +904,33 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
     if (units64 > (int64_t)1 << 30) return -1;
     const int units = (int)units64;
     const int per_xcd = (units + 7) / 8;
-    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS>), dim3(8 * per_xcd),
-                       dim3(Cfg<T, D, DVS>::THREADS), 0, stream, static_cast<const T *>(q),
+    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG>), dim3(8 * per_xcd),
+                       dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
                        initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,
                        snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd);
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <bool SG>
+int launch_dtype(const void *q, const void *k, const void *v, const float *log_alpha,
+                 const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                 void *out, float *final_state, float *snapshots, int snapshot_every,
+                 int num_snapshots, int num_seqs, int seq_len, int total_tokens, int num_heads,
+                 int head_dim, int dtype, hipStream_t stream) {
+    if (dtype == kDtypeBf16) {
+        if (head_dim == 128)
+            return launch<bf16, 128, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
+                                             out, final_state, snapshots, snapshot_every,
+                                             num_snapshots, num_seqs, seq_len, total_tokens,
+                                             num_heads, stream);
+        return launch<bf16, 64, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+                                        final_state, snapshots, snapshot_every, num_snapshots,
+                                        num_seqs, seq_len, total_tokens, num_heads, stream);
+    }
+    return launch<float, 64, 16, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+                                     final_state, snapshots, snapshot_every, num_snapshots,
+                                     num_seqs, seq_len, total_tokens, num_heads, stream);
 }
 
 }  // namespace
@@ -885,20 +940,17 @@ int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *l
                      void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                      int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
-                     hipStream_t stream) {
+                     int scalar_gate, hipStream_t stream) {
     if (!snapshots) snapshot_every = kC, num_snapshots = 0;
-    if (dtype == kDtypeBf16) {
-        if (head_dim == 128)
-            return launch<bf16, 128, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                         final_state, snapshots, snapshot_every, num_snapshots,
-                                         num_seqs, seq_len, total_tokens, num_heads, stream);
-        return launch<bf16, 64, 64>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+    return scalar_gate
+               ? launch_dtype<true>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                     final_state, snapshots, snapshot_every, num_snapshots,
-                                    num_seqs, seq_len, total_tokens, num_heads, stream);
-    }
-    return launch<float, 64, 16>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                 final_state, snapshots, snapshot_every, num_snapshots, num_seqs,
-                                 seq_len, total_tokens, num_heads, stream);
+                                    num_seqs, seq_len, total_tokens, num_heads, head_dim, dtype,
+                                    stream)
+               : launch_dtype<false>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+                                     final_state, snapshots, snapshot_every, num_snapshots,
+                                     num_seqs, seq_len, total_tokens, num_heads, head_dim, dtype,
+                                     stream);
 }
 
 }  // namespace kda

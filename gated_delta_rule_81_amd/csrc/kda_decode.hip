@@ -25,7 +25,9 @@ namespace kda {
 
 // One workgroup (4 waves) per (session, head).  A state row of D floats is
 // held by D/4 lanes, four consecutive key channels each.
-template <typename T, int D>
+// SG: one gate per (session, head) applied to every key channel (the Gated
+// DeltaNet gate); otherwise one per key channel.
+template <typename T, int D, bool SG>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -63,11 +65,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         kf[j] = to_f32(k[vec + 4 * c4 + j]);
         qf[j] = to_f32(q[vec + 4 * c4 + j]);
     }
-    const float4 g4 = *reinterpret_cast<const float4 *>(log_alpha + vec + 4 * c4);
-    af[0] = fast_exp2(g4.x * kLog2e);
-    af[1] = fast_exp2(g4.y * kLog2e);
-    af[2] = fast_exp2(g4.z * kLog2e);
-    af[3] = fast_exp2(g4.w * kLog2e);
+    if constexpr (SG) {
+        const float a = fast_exp2(log_alpha[unit] * kLog2e);
+        af[0] = af[1] = af[2] = af[3] = a;
+    } else {
+        const float4 g4 = *reinterpret_cast<const float4 *>(log_alpha + vec + 4 * c4);
+        af[0] = fast_exp2(g4.x * kLog2e);
+        af[1] = fast_exp2(g4.y * kLog2e);
+        af[2] = fast_exp2(g4.z * kLog2e);
+        af[3] = fast_exp2(g4.w * kLog2e);
+    }
     const float b = beta[unit];
     if (tid < D) s_val[tid] = to_f32(v[vec + tid]);
 
@@ -93,28 +100,39 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     if (tid < D) out[vec + tid] = from_f32<T>(s_out[tid]);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool SG>
 static int launch_decode(const void *q, const void *k, const void *v, const float *log_alpha,
                          const float *beta, float *state, void *out, int64_t units,
                          hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<T, D>), dim3((unsigned)units), dim3(256), 0, stream,
-                       static_cast<const T *>(q), static_cast<const T *>(k),
+    hipLaunchKernelGGL((decode_step_kernel<T, D, SG>), dim3((unsigned)units), dim3(256), 0,
+                       stream, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), log_alpha, beta, state, static_cast<T *>(out));
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
-                       const float *beta, float *state, void *out, int64_t units, int head_dim,
-                       int dtype, hipStream_t stream) {
-    if (units == 0) return 0;
+template <bool SG>
+static int launch_decode_dtype(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta, float *state, void *out,
+                               int64_t units, int head_dim, int dtype, hipStream_t stream) {
     if (dtype == kDtypeBf16) {
-        return head_dim == 128
-                   ? launch_decode<bf16, 128>(q, k, v, log_alpha, beta, state, out, units, stream)
-                   : launch_decode<bf16, 64>(q, k, v, log_alpha, beta, state, out, units, stream);
+        return head_dim == 128 ? launch_decode<bf16, 128, SG>(q, k, v, log_alpha, beta, state,
+                                                              out, units, stream)
+                               : launch_decode<bf16, 64, SG>(q, k, v, log_alpha, beta, state,
+                                                             out, units, stream);
     }
     return head_dim == 128
-               ? launch_decode<float, 128>(q, k, v, log_alpha, beta, state, out, units, stream)
-               : launch_decode<float, 64>(q, k, v, log_alpha, beta, state, out, units, stream);
+               ? launch_decode<float, 128, SG>(q, k, v, log_alpha, beta, state, out, units, stream)
+               : launch_decode<float, 64, SG>(q, k, v, log_alpha, beta, state, out, units, stream);
+}
+
+int launch_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
+                       const float *beta, float *state, void *out, int64_t units, int head_dim,
+                       int dtype, int scalar_gate, hipStream_t stream) {
+    if (units == 0) return 0;
+    return scalar_gate ? launch_decode_dtype<true>(q, k, v, log_alpha, beta, state, out, units,
+                                                   head_dim, dtype, stream)
+                       : launch_decode_dtype<false>(q, k, v, log_alpha, beta, state, out, units,
+                                                    head_dim, dtype, stream);
 }
 
 }  // namespace kda

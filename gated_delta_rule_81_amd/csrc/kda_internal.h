@@ -14,20 +14,22 @@ constexpr int kDtypeBf16 = 1;
 // arguments were already validated.  Returns 0, or -1 if the launch failed.
 int launch_decode_step(const void *q, const void *k, const void *v, const float *log_alpha,
                        const float *beta, float *state, void *out, int64_t units, int head_dim,
-                       int dtype, hipStream_t stream);
+                       int dtype, int scalar_gate, hipStream_t stream);
 
 // Queue the chunked prefill.  Dense when cu_seqlens == NULL (num_seqs = batch
 // sequences of seq_len tokens each); packed otherwise (batch == 1).  With
 // snapshots != NULL the state after every snapshot_every tokens (a positive
 // multiple of 32) of each sequence is also written, at most num_snapshots
-// entries.  Arguments are already validated.  Returns 0, or -1 if the launch
-// failed.
+// entries.  scalar_gate != 0: log_alpha holds one gate per (token, head),
+// [T, H], applied to every key channel (the Gated DeltaNet gate); otherwise
+// [T, H, d_k].  Arguments are already validated.  Returns 0, or -1 if the
+// launch failed.
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                      void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                      int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
-                     hipStream_t stream);
+                     int scalar_gate, hipStream_t stream);
 
 // Tokens per chunk of the prefill; snapshot intervals are multiples of it.
 constexpr int kChunkTokens = 32;

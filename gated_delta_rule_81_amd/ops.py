@@ -42,9 +42,12 @@ def _expect(t, name, dtype, shape, device):
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
               beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, *, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              scalar_gate: bool = False
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked KDA prefill (``kda_chunk_fwd``).
+    """Chunked KDA prefill (``kda_chunk_fwd``; with ``scalar_gate=True``,
+    ``kda_chunk_fwd_scalar_gate``: log_alpha is [B, T, H], one Gated DeltaNet
+    gate per token and head applied to every key channel).
 
     q, k, log_alpha: [B, T, H, d_k]; v: [B, T, H, d_v]; beta: [B, T, H];
     initial_state: [N, H, d_v, d_k] fp32 or None (zeros); cu_seqlens: int32
@@ -63,7 +66,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
     _expect(q, "q", q.dtype, (B, T, H, dk), dev)
     _expect(k, "k", q.dtype, (B, T, H, dk), dev)
     _expect(v, "v", q.dtype, (B, T, H, dv), dev)
-    _expect(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    _expect(log_alpha, "log_alpha", torch.float32,
+            (B, T, H) if scalar_gate else (B, T, H, dk), dev)
     _expect(beta, "beta", torch.float32, (B, T, H), dev)
     if cu_seqlens is not None:
         if cu_seqlens.dim() != 1:
@@ -80,11 +84,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torc
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
     _expect(final_state, "final_state", torch.float32, (N, H, dv, dk), dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib().kda_chunk_fwd(
+    name = "kda_chunk_fwd_scalar_gate" if scalar_gate else "kda_chunk_fwd"
+    rc = getattr(lib(), name)(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
         _ptr(cu_seqlens), _ptr(out), _ptr(final_state), B, T, H, dk, dv,
         N if cu_seqlens is not None else 0, _DTYPES[q.dtype], stream)
-    check(rc, "kda_chunk_fwd")
+    check(rc, name)
     return out, final_state
 
 
@@ -154,9 +159,11 @@ def chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
-                beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None
-                ) -> torch.Tensor:
+                beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                scalar_gate: bool = False) -> torch.Tensor:
     """One decode token per session (``kda_decode_step``), state updated in place.
+    With ``scalar_gate=True`` (``kda_decode_step_scalar_gate``) log_alpha is
+    [B, H]: one Gated DeltaNet gate per session and head.
 
     q, k, log_alpha: [B, H, d_k]; v: [B, H, d_v]; beta: [B, H];
     state: [B, H, d_v, d_k] fp32.  Returns out [B, H, d_v] (dtype of q).
@@ -170,14 +177,15 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: to
         raise TypeError(f"unsupported dtype {q.dtype}")
     _expect(k, "k", q.dtype, (B, H, dk), dev)
     _expect(v, "v", q.dtype, (B, H, dv), dev)
-    _expect(log_alpha, "log_alpha", torch.float32, (B, H, dk), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (B, H) if scalar_gate else (B, H, dk), dev)
     _expect(beta, "beta", torch.float32, (B, H), dev)
     _expect(state, "state", torch.float32, (B, H, dv, dk), dev)
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     _expect(out, "out", q.dtype, (B, H, dv), dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                               _ptr(state), _ptr(out), B, H, dk, dv, _DTYPES[q.dtype], stream)
-    check(rc, "kda_decode_step")
+    name = "kda_decode_step_scalar_gate" if scalar_gate else "kda_decode_step"
+    rc = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                              _ptr(state), _ptr(out), B, H, dk, dv, _DTYPES[q.dtype], stream)
+    check(rc, name)
     return out

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -149,6 +149,25 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
                             int32_t dtype, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_scalar_gate -- kda_chunk_fwd with one gate per (token, head)
+ * applied to every key channel: the Gated DeltaNet update that KDA refines
+ * ([K3-explainer] §四: a scalar forget gate per head, where KDA has one per
+ * channel),  S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T.
+ * It is kda_chunk_fwd with log_alpha[t, h, c] = log_alpha[t, h] for every c.
+ *
+ * Every argument has the meaning, rules and layout of kda_chunk_fwd except
+ *   log_alpha  [B, T, H] fp32 (dense) or [1, T, H] (packed), 4-byte aligned,
+ * with the same numerics contract (finite, a 16-token sum above -80).
+ * Returns KDA_OK or a kda_status error code.
+ */
+int kda_chunk_fwd_scalar_gate(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *beta,
+                              const float *initial_state, const int32_t *cu_seqlens, void *out,
+                              float *final_state, int32_t batch, int32_t seq_len,
+                              int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                              int32_t num_seqs, int32_t dtype, hipStream_t stream);
+
+/*
  * kda_decode_step -- one new token per session against a stored state: the
  * fixed-size read and in-place update that decoding performs instead of
  * appending to a cache ([K3-memory] §2; [Kimi-Linear], the decode discussion).
@@ -168,6 +187,18 @@ int kda_decode_step(const void *q, const void *k, const void *v, const float *lo
                     const float *beta, float *state, void *out, int32_t batch,
                     int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, int32_t dtype,
                     hipStream_t stream);
+
+/*
+ * kda_decode_step_scalar_gate -- kda_decode_step with one gate per (session,
+ * head) applied to every key channel (the Gated DeltaNet update, as for
+ * kda_chunk_fwd_scalar_gate).  Arguments as kda_decode_step except
+ *   log_alpha  [B, H] fp32, 4-byte aligned.
+ * Returns KDA_OK or a kda_status error code.
+ */
+int kda_decode_step_scalar_gate(const void *q, const void *k, const void *v,
+                                const float *log_alpha, const float *beta, float *state,
+                                void *out, int32_t batch, int32_t num_heads, int32_t head_dim_k,
+                                int32_t head_dim_v, int32_t dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char *kda_status_string(int status);

@@ -9,6 +9,7 @@ Contents
     recurrence in fp64 (the definition the GPU path must reproduce).
   * ``kda_snapshots`` -- the same recurrence with the state recorded after
     every N tokens of each sequence.
+  * ``gdn_forward`` -- the scalar-gate (Gated DeltaNet) special case.
   * ``forms.projection_forward`` -- a second fp64 witness that builds the
     explicit d_k x d_k transition matrices of the printed KDA update.
   * ``forms.brute_force_exact`` -- exact-rational evaluation through transition
@@ -185,6 +186,20 @@ def kda_snapshots(q, k, v, log_alpha, beta, every: int, state0=None, seq_start=N
             if j < counts[n]:
                 snaps[base[n] + j] = state[n]
     return out, state, snaps
+
+
+def gdn_forward(q, k, v, log_alpha, beta, state0=None, seq_start=None, threads: int = 0):
+    """Gated DeltaNet in fp64: one gate per (token, head) shared by every key
+    channel, S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+    ([K3-explainer] §四, the scalar-gate form KDA refines).  With Diag(alpha_t)
+    = alpha_t I this is the KDA recurrence with the gate repeated over the
+    channels, so ``kda_forward`` computes it.  log_alpha: [T, H]; everything
+    else as ``kda_forward``."""
+    q = _f64(q)
+    T, H, dk = q.shape
+    g = _f64(log_alpha, (T, H))
+    return kda_forward(q, k, v, np.repeat(g[:, :, None], dk, axis=2), beta, state0=state0,
+                       seq_start=seq_start, threads=threads)
 
 
 def kda_decode_step(q, k, v, log_alpha, beta, state, threads: int = 0):

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_snapshots", "kda_decode_step",
+        ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_scalar_gate",
+         "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_scalar_gate",
          "kda_status_string"])
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3
     for code in range(-7, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
@@ -284,3 +285,44 @@ def test_decode_empty_is_ok():
 
 def test_decode_valid_arguments_reach_device_check():
     assert call_decode(dtype=F32, head_dim_k=64, head_dim_v=64) in (DEVICE, OK)
+
+
+# ---------------------------------------------------------------- scalar-gate variants
+def call_chunk_sg(**kw):
+    a = chunk_args(**kw)
+    return _lib.lib().kda_chunk_fwd_scalar_gate(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"],
+        a["cu_seqlens"], a["out"], a["final_state"], a["batch"], a["seq_len"],
+        a["num_heads"], a["head_dim_k"], a["head_dim_v"], a["num_seqs"], a["dtype"],
+        a["stream"])
+
+
+def test_chunk_scalar_gate_checks():
+    a = chunk_args()
+    assert call_chunk_sg() in (DEVICE, OK)
+    assert call_chunk_sg(log_alpha=None) == NULL
+    assert call_chunk_sg(dtype=F32) == UNSUP
+    # one float per (token, head): 4-byte alignment suffices
+    assert call_chunk_sg(log_alpha=a["log_alpha"] + 4) in (DEVICE, OK)
+    assert call_chunk_sg(log_alpha=a["log_alpha"] + 2) == ALIGN
+    # the gate array is [B, T, H] floats: an output 2*100*3*4 bytes past it is clear
+    assert call_chunk_sg(out=a["log_alpha"] + 2400) in (DEVICE, OK)
+    assert call_chunk_sg(out=a["log_alpha"] + 2384) == ALIAS
+
+
+def call_decode_sg(**kw):
+    a = decode_args(**kw)
+    return _lib.lib().kda_decode_step_scalar_gate(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["state"], a["out"], a["batch"],
+        a["num_heads"], a["head_dim_k"], a["head_dim_v"], a["dtype"], a["stream"])
+
+
+def test_decode_scalar_gate_checks():
+    a = decode_args()
+    assert call_decode_sg() in (DEVICE, OK)
+    assert call_decode_sg(log_alpha=None) == NULL
+    assert call_decode_sg(log_alpha=a["log_alpha"] + 4) in (DEVICE, OK)
+    assert call_decode_sg(log_alpha=a["log_alpha"] + 1) == ALIGN
+    # [B, H] = 4 * 3 floats = 48 bytes
+    assert call_decode_sg(out=a["log_alpha"] + 48) in (DEVICE, OK)
+    assert call_decode_sg(out=a["log_alpha"] + 32) == ALIAS

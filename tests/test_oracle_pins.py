@@ -375,3 +375,24 @@ def test_last_snapshot_is_the_final_state_when_the_interval_divides_the_length()
     # lengths 16 and 96 are multiples of 16: their last snapshots are entries 0 and -1
     assert np.array_equal(snaps[0], fin[2])
     assert np.array_equal(snaps[-1], fin[5])
+
+
+def test_gdn_forward_is_the_scalar_gate_recurrence():
+    """gdn_forward against the Gated DeltaNet update written out with explicit
+    d_k x d_k matrices ([K3-explainer] §四), two heads and two sequences."""
+    rng = np.random.default_rng(21)
+    T, H, dk, dv = 30, 2, 5, 4
+    q, k, v, g, b = _rand_case(rng, T, H, dk, dv)
+    gs = g[:, :, 0]  # one gate per (token, head)
+    starts = [0, 12, 30]
+    S0 = rng.standard_normal((2, H, dv, dk)) * 0.3
+    out, sT = oracle.gdn_forward(q, k, v, gs, b, state0=S0, seq_start=starts)
+    for n in range(2):
+        for h in range(H):
+            S = S0[n, h].T.copy()
+            for t in range(starts[n], starts[n + 1]):
+                kt = k[t, h]
+                S = np.exp(gs[t, h]) * (np.eye(dk) - b[t, h] * np.outer(kt, kt)) @ S \
+                    + b[t, h] * np.outer(kt, v[t, h])
+                assert _rel(out[t, h], S.T @ q[t, h]) < 1e-12
+            assert _rel(sT[n, h], S.T) < 1e-12
