@@ -460,16 +460,26 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         const int c = 4 * (4 * wave + (lane >> 4));
         const int pc = phys<T>(c);
         const ChunkOffsets<T, D, DVS, SG> offs(wave, lane, h, H, v0);
-        ChunkRegs<T, D, DVS, SG> R;
+        auto src = [&](int ci) {
+            const int64_t t0 = tbeg + (int64_t)ci * kC;
+            return chunk_src(q, k, v, log_alpha, beta, t0,
+                             (int)((tend - t0) < kC ? (tend - t0) : kC), H, D, SG);
+        };
+        // Two register sets: the loads of chunk n + 2 go out at the start of
+        // tick n and are staged at the end of tick n + 1, so a load has about
+        // two ticks to land (global loads under this kernel's traffic take
+        // about as long as one tick).
+        ChunkRegs<T, D, DVS, SG> RA, RB;
         if (nchunks > 0) {
-            load_chunk(R, chunk_src(q, k, v, log_alpha, beta, tbeg,
-                                    (int)((tend - tbeg) < kC ? (tend - tbeg) : kC), H, D, SG),
-                       offs, wave, lane);
-            stage_chunk(R, smem, offs, wave, lane);
+            load_chunk(RA, src(0), offs, wave, lane);
+            stage_chunk(RA, smem, offs, wave, lane);
         }
         __syncthreads();
+        if (nchunks > 1) load_chunk(RB, src(1), offs, wave, lane);
 
-        for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
+        // one tick: Rl receives chunk tick + 2, Rs (chunk tick + 1) is staged
+        auto prep_tick = [&](int tick, ChunkRegs<T, D, DVS, SG> &Rl,
+                             ChunkRegs<T, D, DVS, SG> &Rs) {
             const bool on = tick < nchunks;  // prepares chunk `tick`
             unsigned char *PS = smem + (tick & 1) * G::SET;
             T *pKP = reinterpret_cast<T *>(PS + G::sKP);
@@ -484,15 +494,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 
             // ------------------------------------------------------ phase 1
             if (on) {
-                // the next chunk's loads go out first: they land while this chunk
-                // is prepared and are staged at the end of phase 2
-                if (tick + 1 < nchunks) {
-                    const int64_t ntok0 = tbeg + (int64_t)(tick + 1) * kC;
-                    load_chunk(R, chunk_src(q, k, v, log_alpha, beta, ntok0,
-                                            (int)((tend - ntok0) < kC ? (tend - ntok0) : kC), H,
-                                            D, SG),
-                               offs, wave, lane);
-                }
+                // the loads of chunk tick + 2 go out first (staged next tick)
+                if (tick + 2 < nchunks) load_chunk(Rl, src(tick + 2), offs, wave, lane);
                 // this chunk's rows r and r + 16 from the staging area
                 Raw<G::RW> rk[2], rq[2];
                 float d0[4], d1[4], erho[4];  // gates of rows r, r + 16 (channels c .. c + 3)
@@ -648,6 +651,10 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // tiles 0-5 = A_00 (then T_00), A_11 (then T_11), A_10, Mqk_00,
             // Mqk_11, Mqk_10; wave w takes tiles w and w + PW (products over
             // physical channels, both operands in the same order)
+            // the waves without a diagonal tile hold back briefly, so the LDS
+            // reads of the two diagonal tiles (the head of the substitution
+            // chain, the longest path of this phase) are served first
+            if (wave >= 2) __builtin_amdgcn_s_sleep(2);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tile = wave + u * G::PW;
@@ -723,9 +730,12 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 }
             }
             // the next chunk's rows, loaded during phase 1, into the staging area
-            if (tick + 1 < nchunks) stage_chunk(R, smem, offs, wave, lane);
+            if (tick + 1 < nchunks) stage_chunk(Rs, smem, offs, wave, lane);
             __syncthreads();
-
+        };
+        for (int tick = 0; nchunks > 0 && tick <= nchunks; tick += 2) {
+            prep_tick(tick, RA, RB);
+            if (tick + 1 <= nchunks) prep_tick(tick + 1, RB, RA);
         }
         return;
     }
