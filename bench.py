@@ -114,6 +114,48 @@ def cpu_baseline(inp, heads, threads):
                       f"fp64, {dt:.1f} s; value = sample token-heads/s / {H} heads"}
 
 
+def attainable_peaks(torch):
+    """Measured ceilings to set beside the published ones: HBM bandwidth of a
+    4 GiB device-to-device copy (bytes read + written per second) and bf16
+    TFLOP/s of an 8192^3 GEMM from the vendor BLAS (calibration only; no part
+    of the KDA path uses either)."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30  # 4 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    y = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2 * m ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    log(f"copy {copy_gbs:.0f} GB/s ({copy_gbs / HBM_PEAK_GBS:.1%} of published); "
+        f"bf16 GEMM {tflops:.0f} TFLOP/s ({tflops / BF16_DENSE_PEAK_TFLOPS:.1%} of published)")
+    return {"metric": "attainable peaks (calibration)", "hbm_copy_gbs": copy_gbs,
+            "hbm_published_gbs": HBM_PEAK_GBS, "bf16_gemm_tflops": tflops,
+            "bf16_published_tflops": BF16_DENSE_PEAK_TFLOPS,
+            "copy": "4 GiB fp32 device-to-device, read + write bytes",
+            "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +166,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="time kda_chunk_fwd only (for counter passes); no decode fields")
+    ap.add_argument("--attainable", action="store_true",
+                    help="measure attainable peaks instead (device-to-device copy for HBM, a "
+                         "large bf16 GEMM for the matrix cores) and print them as one JSON line")
     ap.add_argument("--scalar-gate", action="store_true",
                     help="time the scalar-gate (Gated DeltaNet) entry points, one gate per "
                          "token and head (the first channel of the seeded gates)")
@@ -139,6 +184,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.attainable:
+        print(json.dumps(attainable_peaks(torch)), flush=True)
+        return
 
     import synth
     import gated_delta_rule_81_amd as kda
