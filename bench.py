@@ -24,6 +24,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
        [--skip-decode]        (decode workload shrunk to one session-head; for
                                counter passes on kda_chunk_fwd only)
+       [--segments G [--seg-workload long_1m|prefill_4k]]
+                              (instead: kda_chunk_fwd_segmented with G requested
+                               segments on one long sequence, kda_chunk_fwd
+                               timed beside it; its own JSON line)
 """
 from __future__ import annotations
 
@@ -156,6 +160,77 @@ def attainable_peaks(torch):
             "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
 
 
+def bench_segmented(torch, args):
+    """kda_chunk_fwd_segmented on one long sequence (B=1), inputs drawn on the
+    device, with kda_chunk_fwd on the same input timed beside it."""
+    import synth
+    import gated_delta_rule_81_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.seg_workload]
+    log("generating on the device:", w.notes)
+    P = synth.prefill_inputs(w, device=dev)
+    T, H, D = w.seq_len, w.heads, w.head_dim
+    G = args.segments
+    out = torch.empty_like(P["v"])
+    fin = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.segmented_workspace_size(T, H, D, G), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def seg():
+        kda.chunk_fwd_segmented(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], G,
+                                P["initial_state"], workspace=ws, out=out, final_state=fin)
+
+    def plain():
+        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], P["initial_state"],
+                      out=out, final_state=fin)
+
+    def timed(fn, name, K):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        log(f"timing {K} x {name}")
+        ev[0].record(stream)
+        for s in range(K):
+            fn()
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
+        log(f"{name}: avg {sum(ms) / K:.3f} ms (min {min(ms):.3f})")
+        return sum(ms) / K, min(ms)
+
+    t0 = time.perf_counter()
+    seg_avg, seg_min = timed(seg, f"kda_chunk_fwd_segmented G={G}", args.steps)
+    wall = time.perf_counter() - t0
+    plain_avg, plain_min = timed(plain, "kda_chunk_fwd", max(1, min(args.steps, 5)))
+    pbytes = prefill_bytes(T, H, D, 1)
+    gbs = pbytes / (seg_avg * 1e-3) / 1e9
+    seg_tokens = 32 * -(-(-(-T // G)) // 32)  # ceil(T / G) rounded up to whole chunks
+    n_seg = -(-T // seg_tokens)
+    return {
+        "metric": f"KDA segmented prefill tokens/s (B=1 H={H} T={T} d={D})",
+        "value": T / (seg_avg * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (wall / args.steps) * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (drawn on the device, seeded)",
+        "config": {"workload": f"kda_chunk_fwd_segmented {w.name}: {w.notes}",
+                   "requested_segments": G, "segments": n_seg,
+                   "segment_tokens": seg_tokens},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "note": "algorithmic bytes of one prefill over the whole segmented "
+                             "call (its three passes read the inputs about three times)"},
+        "segmented_ms_avg": seg_avg, "segmented_ms_min": seg_min,
+        "chunk_fwd_ms_avg": plain_avg, "chunk_fwd_ms_min": plain_min,
+        "speedup_vs_chunk_fwd": plain_avg / seg_avg,
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +250,11 @@ def main():
     ap.add_argument("--snapshot-every", type=int, default=0,
                     help="time kda_chunk_fwd_snapshots with a state snapshot every N tokens "
                          "(a multiple of 32) instead of kda_chunk_fwd")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="time kda_chunk_fwd_segmented with this many requested segments "
+                         "on one long sequence instead (kda_chunk_fwd timed beside it)")
+    ap.add_argument("--seg-workload", default="long_1m", choices=["long_1m", "prefill_4k"],
+                    help="the sequence --segments runs on")
     args = ap.parse_args()
     if args.scalar_gate and args.snapshot_every:
         ap.error("--scalar-gate and --snapshot-every time different entry points; pick one")
@@ -187,6 +267,9 @@ def main():
 
     if args.attainable:
         print(json.dumps(attainable_peaks(torch)), flush=True)
+        return
+    if args.segments > 0:
+        print(json.dumps(bench_segmented(torch, args)), flush=True)
         return
 
     import synth

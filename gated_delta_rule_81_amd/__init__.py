@@ -7,6 +7,8 @@ Python front end of ``libkda.so``; the C ABI is declared in include/kda.h.
     out = decode_step(q, k, v, log_alpha, beta, state)   # state updated in place
 """
 from ._lib import KdaError, lib
-from .ops import chunk_fwd, chunk_fwd_snapshots, decode_step
+from .ops import (chunk_fwd, chunk_fwd_segmented, chunk_fwd_snapshots, decode_step,
+                  segmented_workspace_size)
 
-__all__ = ["chunk_fwd", "chunk_fwd_snapshots", "decode_step", "KdaError", "lib"]
+__all__ = ["chunk_fwd", "chunk_fwd_segmented", "chunk_fwd_snapshots", "decode_step",
+           "segmented_workspace_size", "KdaError", "lib"]

@@ -20,7 +20,7 @@ STATUS = {
 }
 
 # Exported symbols and their C signatures, in include/kda.h order.
-_vp, _fp, _i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32
+_vp, _fp, _i32, _i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 SIGNATURES = {
     "kda_chunk_fwd": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp,
                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
@@ -29,6 +29,10 @@ SIGNATURES = {
                                  _vp], ctypes.c_int),
     "kda_chunk_fwd_scalar_gate": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp,
                                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "kda_chunk_fwd_segmented": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp,
+                                 _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp],
+                                ctypes.c_int),
+    "kda_chunk_fwd_segmented_workspace_size": ([_i32, _i32, _i32, _i32], _i64),
     "kda_decode_step_scalar_gate": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "kda_decode_step": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,

@@ -79,7 +79,7 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
                    void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                    int32_t num_snapshots, int32_t batch, int32_t seq_len, int32_t num_heads,
                    int32_t head_dim_k, int32_t head_dim_v, int32_t num_seqs, int32_t dtype,
-                   bool scalar_gate, hipStream_t stream) {
+                   bool scalar_gate, hipStream_t stream, bool check_only = false) {
     // sizes
     if (batch < 0 || seq_len < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0)
         return KDA_ERR_SHAPE;
@@ -132,6 +132,7 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
             continue;  // in-place state update is allowed
         if (overlap(rs1, inputs[i])) return KDA_ERR_ALIAS;
     }
+    if (check_only) return KDA_OK;
     if (nseq == 0 || num_heads == 0) return KDA_OK;
     const int st = check_device();
     if (st != KDA_OK) return st;
@@ -139,7 +140,7 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
                                          final_state, num_snapshots > 0 ? snapshots : nullptr,
                                          snapshot_every, num_snapshots, (int32_t)nseq, seq_len,
                                          (int32_t)tokens, num_heads, d, dtype, scalar_gate ? 1 : 0,
-                                         stream);
+                                         0, stream);
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -177,9 +178,96 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+// Segment plan of the segmented prefill: segments of seg_len tokens (a
+// multiple of the chunk length, at least one chunk), nseg of them (0 for T = 0).
+struct SegPlan {
+    int seg_len, nseg;
+};
+SegPlan seg_plan(int32_t seq_len, int32_t num_segments) {
+    if (seq_len <= 0) return {kda::kChunkTokens, 0};
+    int64_t L = ((int64_t)seq_len + num_segments - 1) / num_segments;
+    L = (L + kda::kChunkTokens - 1) / kda::kChunkTokens * kda::kChunkTokens;
+    return {(int)L, (int)(((int64_t)seq_len + L - 1) / L)};
+}
+// Workspace: segment offsets (padded to 256 bytes), then four [nseg, H, D, D]
+// fp32 arrays: the segments' maps Y (from S = 0) and X (from S = I, zero
+// values), their entering states and their final states.
+uint64_t seg_cu_bytes(int nseg) { return ((uint64_t)(nseg + 1) * 4 + 255) / 256 * 256; }
+uint64_t seg_state_bytes(int nseg, int H, int d) { return (uint64_t)nseg * H * d * d * 4; }
+
 }  // namespace
 
 extern "C" {
+
+int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_heads,
+                                               int32_t head_dim, int32_t num_segments) {
+    if (seq_len < 0 || num_heads < 0 || num_segments < 1 || (head_dim != 64 && head_dim != 128))
+        return -1;
+    const SegPlan sp = seg_plan(seq_len, num_segments);
+    return (int64_t)(seg_cu_bytes(sp.nseg) + 4 * seg_state_bytes(sp.nseg, num_heads, head_dim));
+}
+
+int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, int32_t seq_len, int32_t num_heads,
+                            int32_t head_dim_k, int32_t head_dim_v, int32_t num_segments,
+                            int32_t dtype, void *workspace, int64_t workspace_bytes,
+                            hipStream_t stream) {
+    if (num_segments < 1 || workspace_bytes < 0) return KDA_ERR_SHAPE;
+    // every kda_chunk_fwd rule for one dense sequence
+    int st = chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, nullptr, out, final_state,
+                            nullptr, 0, 0, 1, seq_len, num_heads, head_dim_k, head_dim_v, 0,
+                            dtype, false, stream, true);
+    if (st != KDA_OK) return st;
+    const SegPlan sp = seg_plan(seq_len, num_segments);
+    if (sp.nseg <= 1 || num_heads == 0)  // nothing to split: the plain prefill
+        return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, nullptr, out,
+                              final_state, nullptr, 0, 0, 1, seq_len, num_heads, head_dim_k,
+                              head_dim_v, 0, dtype, false, stream);
+    const int d = head_dim_k;
+    const uint64_t cu_b = seg_cu_bytes(sp.nseg), sb = seg_state_bytes(sp.nseg, num_heads, d);
+    const uint64_t need = cu_b + 4 * sb;
+    if (!workspace) return KDA_ERR_NULL;
+    if ((uint64_t)workspace_bytes < need) return KDA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return KDA_ERR_ALIGN;
+    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
+    const uint64_t th = (uint64_t)seq_len * num_heads, hs = (uint64_t)num_heads * d * d * 4;
+    const Range rw{workspace, need};
+    const Range others[] = {{q, th * d * esz}, {k, th * d * esz}, {v, th * d * esz},
+                            {log_alpha, th * d * 4}, {beta, th * 4}, {initial_state, hs},
+                            {out, th * d * esz}, {final_state, hs}};
+    for (const Range &r : others)
+        if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    st = check_device();
+    if (st != KDA_OK) return st;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    int32_t *cu = reinterpret_cast<int32_t *>(ws);
+    float *Y = reinterpret_cast<float *>(ws + cu_b);
+    float *X = reinterpret_cast<float *>(ws + cu_b + sb);
+    float *Min = reinterpret_cast<float *>(ws + cu_b + 2 * sb);
+    float *Fin = reinterpret_cast<float *>(ws + cu_b + 3 * sb);
+    const int T = seq_len, n = sp.nseg;
+    int rc = kda::launch_segment_bounds(cu, n, sp.seg_len, T, stream);
+    // each segment's map from a zero state (Y) and, with zero values, from the
+    // identity (X), no outputs
+    if (rc == 0)
+        rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, nullptr, cu, nullptr, Y, nullptr, 0,
+                                   0, n, T, T, num_heads, d, dtype, 0, 0, stream);
+    if (rc == 0)
+        rc = kda::launch_chunk_fwd(q, k, nullptr, log_alpha, beta, nullptr, cu, nullptr, X,
+                                   nullptr, 0, 0, n, T, T, num_heads, d, dtype, 0, 1, stream);
+    // the entering state of every segment, then the segments from their true
+    // entering states
+    if (rc == 0) rc = kda::launch_segment_fold(initial_state, X, Y, Min, n, num_heads, d, stream);
+    if (rc == 0)
+        rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, Min, cu, out, Fin, nullptr, 0, 0, n,
+                                   T, T, num_heads, d, dtype, 0, 0, stream);
+    if (rc == 0 && final_state &&
+        hipMemcpyAsync(final_state, Fin + (uint64_t)(n - 1) * num_heads * d * d, hs,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        rc = -1;
+    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,

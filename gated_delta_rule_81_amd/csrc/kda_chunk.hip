@@ -164,7 +164,9 @@ __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v
                                             kRsrcWord3);
     s.q = __builtin_amdgcn_make_buffer_rsrc((void *)(q + e0), 0, elems * (int)sizeof(T),
                                             kRsrcWord3);
-    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, elems * (int)sizeof(T),
+    // v == NULL reads as zero values: a descriptor covering no bytes
+    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v ? v + e0 : v), 0,
+                                            v ? elems * (int)sizeof(T) : 0,
                                             kRsrcWord3);
     s.g = scalar_gate ? __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + tok0 * H), 0,
                                                           nvalid * H * 4, kRsrcWord3)
@@ -398,8 +400,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
     T *__restrict__ out, float *__restrict__ final_state, float *__restrict__ snapshots,
-    int snap_every, int snap_cap, int num_seqs, int seq_len, int total_tokens, int H, int units,
-    int units_per_xcd) {
+    int snap_every, int snap_cap, int init_identity, int num_seqs, int seq_len, int total_tokens,
+    int H, int units, int units_per_xcd) {
     typedef Cfg<T, D, DVS, SG> G;
     typedef Mma<T> M;
     typedef ScanMma<T> SM;
@@ -772,9 +774,14 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     f32x4 Sm[G::NRT];
 #pragma unroll
     for (int t = 0; t < G::NRT; ++t)
-        Sm[t] = initial_state ? *reinterpret_cast<const f32x4 *>(
-                                    initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * l4)
-                              : zero4();
+        Sm[t] = init_identity
+                    ? f32x4{vcol == 16 * t + 4 * l4 ? 1.f : 0.f, vcol == 16 * t + 4 * l4 + 1 ? 1.f : 0.f,
+                            vcol == 16 * t + 4 * l4 + 2 ? 1.f : 0.f,
+                            vcol == 16 * t + 4 * l4 + 3 ? 1.f : 0.f}
+                : initial_state ? *reinterpret_cast<const f32x4 *>(initial_state + sbase +
+                                                                  (int64_t)vcol * D + 16 * t +
+                                                                  4 * l4)
+                                : zero4();
     __syncthreads();
 
     for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
@@ -837,11 +844,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 for (int e = 0; e < 4; ++e) r1[e] = b1[e] * X[1][e] - ad[e];
                 Dl[1] = mm16<T>(zero4(), cT3 + 2 * T16, G::LDTT, r1, lane);
             }
-            // O = Q+ S + Mqk Delta (Mqk lower triangular)
+            // O = Q+ S + Mqk Delta (Mqk lower triangular); out == NULL: states only
             const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
             const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < 2 && out; ++rt) {
                 PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 0, lane), Db0);
                 if (sizeof(T) == 4 && rt == 1)
                     PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 1, lane), Db1);
@@ -858,7 +865,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // the chunk's O rows (32 x DVS), whole rows in 16-byte pieces
             constexpr int LV = G::RBV / 16;
 #pragma unroll
-            for (int i = 0; i < G::IO; ++i) {
+            for (int i = 0; i < G::IO && out; ++i) {
                 const int p = (ct * G::IO + i) * 64 + lane, orow = p / LV, b = 16 * (p % LV);
                 if (orow < nvalid)
                     *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(
@@ -907,8 +914,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 template <typename T, int D, int DVS, bool SG>
 int launch(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
            const float *initial_state, const int32_t *cu_seqlens, void *out, float *final_state,
-           float *snapshots, int snap_every, int snap_cap, int num_seqs, int seq_len,
-           int total_tokens, int H, hipStream_t stream) {
+           float *snapshots, int snap_every, int snap_cap, int init_identity, int num_seqs,
+           int seq_len, int total_tokens, int H, hipStream_t stream) {
     const int64_t units64 = (int64_t)num_seqs * H * (D / DVS);
     if (units64 == 0) return 0;
     if (units64 > (int64_t)1 << 30) return -1;
@@ -918,7 +925,8 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
                        dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
                        initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,
-                       snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd);
+                       snap_every, snap_cap, init_identity, num_seqs, seq_len, total_tokens, H,
+                       units, per_xcd);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -926,21 +934,23 @@ template <bool SG>
 int launch_dtype(const void *q, const void *k, const void *v, const float *log_alpha,
                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                  void *out, float *final_state, float *snapshots, int snapshot_every,
-                 int num_snapshots, int num_seqs, int seq_len, int total_tokens, int num_heads,
-                 int head_dim, int dtype, hipStream_t stream) {
+                 int num_snapshots, int init_identity, int num_seqs, int seq_len,
+                 int total_tokens, int num_heads, int head_dim, int dtype, hipStream_t stream) {
     if (dtype == kDtypeBf16) {
         if (head_dim == 128)
             return launch<bf16, 128, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
                                              out, final_state, snapshots, snapshot_every,
-                                             num_snapshots, num_seqs, seq_len, total_tokens,
-                                             num_heads, stream);
+                                             num_snapshots, init_identity, num_seqs, seq_len,
+                                             total_tokens, num_heads, stream);
         return launch<bf16, 64, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                         final_state, snapshots, snapshot_every, num_snapshots,
-                                        num_seqs, seq_len, total_tokens, num_heads, stream);
+                                        init_identity, num_seqs, seq_len, total_tokens, num_heads,
+                                        stream);
     }
     return launch<float, 64, 16, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                      final_state, snapshots, snapshot_every, num_snapshots,
-                                     num_seqs, seq_len, total_tokens, num_heads, stream);
+                                     init_identity, num_seqs, seq_len, total_tokens, num_heads,
+                                     stream);
 }
 
 }  // namespace
@@ -950,17 +960,17 @@ int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *l
                      void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                      int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
-                     int scalar_gate, hipStream_t stream) {
+                     int scalar_gate, int init_identity, hipStream_t stream) {
     if (!snapshots) snapshot_every = kC, num_snapshots = 0;
     return scalar_gate
                ? launch_dtype<true>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                     final_state, snapshots, snapshot_every, num_snapshots,
-                                    num_seqs, seq_len, total_tokens, num_heads, head_dim, dtype,
-                                    stream)
+                                    init_identity, num_seqs, seq_len, total_tokens, num_heads,
+                                    head_dim, dtype, stream)
                : launch_dtype<false>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                      final_state, snapshots, snapshot_every, num_snapshots,
-                                     num_seqs, seq_len, total_tokens, num_heads, head_dim, dtype,
-                                     stream);
+                                     init_identity, num_seqs, seq_len, total_tokens, num_heads,
+                                     head_dim, dtype, stream);
 }
 
 }  // namespace kda

@@ -22,16 +22,29 @@ int launch_decode_step(const void *q, const void *k, const void *v, const float 
 // multiple of 32) of each sequence is also written, at most num_snapshots
 // entries.  scalar_gate != 0: log_alpha holds one gate per (token, head),
 // [T, H], applied to every key channel (the Gated DeltaNet gate); otherwise
-// [T, H, d_k].  Arguments are already validated.  Returns 0, or -1 if the
-// launch failed.
+// [T, H, d_k].  init_identity != 0: every workgroup starts from S = I instead
+// of initial_state (d_k == d_v), which turns the final state into the chunk
+// sequence's state transition when v == NULL (v == NULL reads as zeros).
+// Arguments are already validated.  Returns 0, or -1 if the launch failed.
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                      void *out, float *final_state, float *snapshots, int32_t snapshot_every,
                      int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
-                     int scalar_gate, hipStream_t stream);
+                     int scalar_gate, int init_identity, hipStream_t stream);
 
 // Tokens per chunk of the prefill; snapshot intervals are multiples of it.
 constexpr int kChunkTokens = 32;
+
+// Segmented prefill of one sequence.  cu[g] = min(g * seg_len, total) for
+// g = 0 .. nseg (the segment boundaries as packed-sequence offsets).
+int launch_segment_bounds(int32_t *cu, int nseg, int seg_len, int total, hipStream_t stream);
+
+// Entering states of the segments, [nseg, H, D, D] in the stored orientation
+// M = S^T: m_in[0] = m0 (zero when m0 == NULL), m_in[g + 1] = m_in[g] X[g] + Y[g]
+// (X[g], Y[g]: the final states of segment g from S = I with zero values and
+// from S = 0).  head_dim is 64 or 128.  Returns 0, or -1 if the launch failed.
+int launch_segment_fold(const float *m0, const float *X, const float *Y, float *m_in, int nseg,
+                        int H, int head_dim, hipStream_t stream);
 
 }  // namespace kda

@@ -5,7 +5,8 @@ Every step of the computation runs in the HIP kernels behind the C ABI
 torch (device memory) and passes raw pointers plus torch's current stream.
 
 Pages cited (by title):
-  [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (§四: the update).
+  [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (§四: the update;
+                  §六.2: a chunk's updates as one transition matrix).
   [K3-memory]     "Kimi K3 Changed the Memory Math for Agentic AI Forever" (§3:
                   the [batch, heads, value_dim, key_dim] state layout).
 """
@@ -156,6 +157,66 @@ def chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         B, T, H, dk, dv, N if cu_seqlens is not None else 0, _DTYPES[q.dtype], stream)
     check(rc, "kda_chunk_fwd_snapshots")
     return out, final_state, snapshots
+
+
+def segmented_workspace_size(seq_len: int, num_heads: int, head_dim: int,
+                             num_segments: int) -> int:
+    """Bytes of workspace ``chunk_fwd_segmented`` needs
+    (``kda_chunk_fwd_segmented_workspace_size``)."""
+    n = lib().kda_chunk_fwd_segmented_workspace_size(seq_len, num_heads, head_dim, num_segments)
+    if n < 0:
+        raise ValueError(f"invalid sizes seq_len={seq_len} num_heads={num_heads} "
+                         f"head_dim={head_dim} num_segments={num_segments}")
+    return int(n)
+
+
+def chunk_fwd_segmented(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        log_alpha: torch.Tensor, beta: torch.Tensor, num_segments: int,
+                        initial_state: Optional[torch.Tensor] = None, *,
+                        workspace: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` of one long sequence (B = 1, no cu_seqlens) split into
+    ``num_segments`` segments that run in parallel (``kda_chunk_fwd_segmented``):
+    per-segment state maps, a fold over the segments, then every segment again
+    from its entering state ([K3-explainer] §六.2, the chunk transition).
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``segmented_workspace_size(T, H, d_k, num_segments)`` bytes (allocated here
+    when None).  Returns (out [1, T, H, d_v], final_state [1, H, d_v, d_k] or None).
+    """
+    if q.dim() != 4 or q.shape[0] != 1:
+        raise ValueError("q must be [1, T, H, d_k]")
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _expect(q, "q", q.dtype, (1, T, H, dk), dev)
+    _expect(k, "k", q.dtype, (1, T, H, dk), dev)
+    _expect(v, "v", q.dtype, (1, T, H, dv), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (1, T, H, dk), dev)
+    _expect(beta, "beta", torch.float32, (1, T, H), dev)
+    _expect(initial_state, "initial_state", torch.float32, (1, H, dv, dk), dev)
+    need = segmented_workspace_size(T, H, dk, int(num_segments))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _expect(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    if out is None:
+        out = torch.empty((1, T, H, dv), dtype=q.dtype, device=dev)
+    _expect(out, "out", q.dtype, (1, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((1, H, dv, dk), dtype=torch.float32, device=dev)
+    _expect(final_state, "final_state", torch.float32, (1, H, dv, dk), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_chunk_fwd_segmented(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(out), _ptr(final_state), T, H, dk, dv, int(num_segments), _DTYPES[q.dtype],
+        _ptr(workspace), workspace.numel(), stream)
+    check(rc, "kda_chunk_fwd_segmented")
+    return out, final_state
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -166,6 +166,56 @@ int kda_chunk_fwd_scalar_gate(const void *q, const void *k, const void *v,
                               float *final_state, int32_t batch, int32_t seq_len,
                               int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
                               int32_t num_seqs, int32_t dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_segmented -- kda_chunk_fwd of ONE long sequence (batch 1, no
+ * cu_seqlens) split into segments that run side by side, for the long-context
+ * prefill ([Kimi-Linear] Fig. 7: batch 1 up to 1M tokens) where a few heads
+ * leave most of the GPU idle while one chain of chunks runs in order.
+ *
+ * A run of chunks maps its entering state affinely, S_out = P S_in + R, with P
+ * the product of the chunks' transitions ([K3-explainer] §六.2: a chunk's
+ * rank-one updates collapse into one transition matrix, P = D - K W^T).  The
+ * call (1) computes every segment's R (the segment from S = 0) and P (from
+ * S = I with zero values) in one launch each, all segments and heads in
+ * parallel, (2) folds the maps in segment order to get each segment's true
+ * entering state, and (3) reruns every segment from that state, writing out.
+ * The result is kda_chunk_fwd's up to rounding order, at about three times
+ * its arithmetic and reads.
+ *
+ * Arguments as kda_chunk_fwd with batch = 1 and cu_seqlens = NULL, plus
+ *   num_segments     >= 1 (else KDA_ERR_SHAPE): the requested split.  Segments
+ *                    hold L = 32 * ceil(ceil(seq_len / num_segments) / 32)
+ *                    tokens (the last one the rest), so ceil(seq_len / L) of
+ *                    them run; when that is 1 the call is kda_chunk_fwd and
+ *                    the workspace is not touched.
+ *   workspace        caller-owned device scratch, 256-byte aligned (else
+ *                    KDA_ERR_ALIGN), of at least
+ *                    kda_chunk_fwd_segmented_workspace_size(seq_len,
+ *                    num_heads, head_dim_k, num_segments) bytes (else
+ *                    KDA_ERR_SHAPE); NULL (KDA_ERR_NULL) only where it is not
+ *                    touched.  It must not overlap any argument array
+ *                    (KDA_ERR_ALIAS); its contents on return are unspecified.
+ *   workspace_bytes  its size in bytes.
+ * Calls that share a workspace must not run concurrently.
+ * Returns KDA_OK or a kda_status error code.
+ */
+int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *log_alpha,
+                            const float *beta, const float *initial_state, void *out,
+                            float *final_state, int32_t seq_len, int32_t num_heads,
+                            int32_t head_dim_k, int32_t head_dim_v, int32_t num_segments,
+                            int32_t dtype, void *workspace, int64_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Bytes of workspace kda_chunk_fwd_segmented needs for these sizes: the
+ * segment offsets (padded to 256 bytes) and four fp32 arrays of
+ * n_seg * num_heads * head_dim^2 (two maps, entering and leaving states).
+ * -1 for seq_len < 0, num_heads < 0, num_segments < 1 or head_dim not 64/128.
+ * Host only; touches no device.
+ */
+int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_heads,
+                                               int32_t head_dim, int32_t num_segments);
 
 /*
  * kda_decode_step -- one new token per session against a stored state: the

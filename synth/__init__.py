@@ -59,6 +59,8 @@ WORKLOADS = {
     "varlen_16": Workload("varlen_16", heads=32, head_dim=128, dtype="bf16", seed=3,
                           n_seqs=16, len_range=(1024, 65536), init_std=0.02,
                           notes="16 packed sequences, lengths U[1024,65536], H=32"),
+    "long_1m": Workload("long_1m", heads=32, head_dim=128, dtype="bf16", seed=5,
+                        seq_len=1 << 20, notes="B=1 H=32 T=1,048,576 d=128 bf16, zero state"),
     "decode_b256": Workload("decode_b256", heads=96, head_dim=128, dtype="bf16", seed=4,
                             batch=256, steps=64, init_std=0.02,
                             notes="B=256 sessions H=96 d=128, 64 single-token steps"),
@@ -74,15 +76,18 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
 
 
 def _draw(gen, shape, H, d, dtype, init_std, n_states):
-    """q, k, v, beta, log_alpha for ``shape`` = leading dims (e.g. (B, T))."""
-    q = _unit(torch.randn(*shape, H, d, generator=gen)).to(dtype)
-    k = _unit(torch.randn(*shape, H, d, generator=gen)).to(dtype)
-    v = torch.randn(*shape, H, d, generator=gen).to(dtype)
-    beta = torch.sigmoid(torch.randn(*shape, H, generator=gen))
-    log_alpha = -torch.nn.functional.softplus(torch.randn(*shape, H, d, generator=gen) - 4.0)
+    """q, k, v, beta, log_alpha for ``shape`` = leading dims (e.g. (B, T)),
+    on the generator's device."""
+    dev = gen.device
+    q = _unit(torch.randn(*shape, H, d, generator=gen, device=dev)).to(dtype)
+    k = _unit(torch.randn(*shape, H, d, generator=gen, device=dev)).to(dtype)
+    v = torch.randn(*shape, H, d, generator=gen, device=dev).to(dtype)
+    beta = torch.sigmoid(torch.randn(*shape, H, generator=gen, device=dev))
+    log_alpha = -torch.nn.functional.softplus(
+        torch.randn(*shape, H, d, generator=gen, device=dev) - 4.0)
     state = None
     if init_std > 0:
-        state = torch.randn(n_states, H, d, d, generator=gen) * init_std
+        state = torch.randn(n_states, H, d, d, generator=gen, device=dev) * init_std
     return q, k, v, beta, log_alpha, state
 
 
@@ -104,12 +109,15 @@ def sequence_inputs(w: Workload, n: int):
     return dict(q=q, k=k, v=v, beta=beta, log_alpha=g, initial_state=s)
 
 
-def prefill_inputs(w, **overrides):
+def prefill_inputs(w, device=None, **overrides):
     """CPU tensors for one prefill workload.
 
     ``w`` is a ``Workload`` or a key of ``WORKLOADS``; keyword overrides replace
     Workload fields (e.g. ``seq_len=300`` or ``heads=3``) for smaller cases
-    with the same distributions.
+    with the same distributions.  ``device`` (dense workloads only) draws the
+    tensors there with that device's own generator seeded the same way: same
+    distributions and a reproducible draw, but not the CPU draw's numbers (the
+    long workloads are too large to draw on the host in reasonable time).
 
     Dense: q, k, log_alpha [B, T, H, d]; v [B, T, H, d]; beta [B, T, H];
            initial_state [B, H, d, d] or None; cu_seqlens None.
@@ -121,6 +129,8 @@ def prefill_inputs(w, **overrides):
     if overrides:
         w = replace(w, **overrides)
     dt = _torch_dtype(w.dtype)
+    if device is not None and w.n_seqs:
+        raise ValueError("device draws are for dense workloads")
     if w.n_seqs:
         lengths, _ = varlen_lengths(w)
         # Sequences are independent draws: generate them on parallel threads
@@ -139,7 +149,7 @@ def prefill_inputs(w, **overrides):
         out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32)
         out["workload"] = w
         return out
-    gen = torch.Generator().manual_seed(w.seed)
+    gen = torch.Generator(device=device or "cpu").manual_seed(w.seed)
     q, k, v, beta, g, s = _draw(gen, (w.batch, w.seq_len), w.heads, w.head_dim, dt,
                                 w.init_std, w.batch)
     return dict(q=q, k=k, v=v, beta=beta, log_alpha=g, initial_state=s,

@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_scalar_gate",
+         "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_size",
          "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_scalar_gate",
          "kda_status_string"])
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 3
+    assert L.kda_abi_version() == 4
     for code in range(-7, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
@@ -226,6 +227,72 @@ def test_snapshots_share_the_chunk_fwd_checks():
     assert call_snap(q=None) == NULL
     assert call_snap(dtype=F32) == UNSUP
     assert call_snap(batch=0) == OK
+
+
+# ---------------------------------------------------------------- chunk_fwd_segmented
+def seg_size(T, H, D, G):
+    return _lib.lib().kda_chunk_fwd_segmented_workspace_size(T, H, D, G)
+
+
+def test_segmented_workspace_size():
+    st = lambda n, H, D: n * H * D * D * 4
+    # 1000 tokens in 4 requested segments: 256-token segments, 4 of them
+    assert seg_size(1000, 3, 128, 4) == 256 + 4 * st(4, 3, 128)
+    # 100 tokens in 8: segments of one chunk (32 tokens), 4 of them
+    assert seg_size(100, 2, 64, 8) == 256 + 4 * st(4, 2, 64)
+    # 65 offsets need 260 bytes, padded to 512
+    assert seg_size(64 * 32, 1, 64, 64) == 512 + 4 * st(64, 1, 64)
+    assert seg_size(0, 3, 128, 4) == 256
+    assert seg_size(5000, 0, 128, 4) == 256
+    for bad in [(-1, 3, 128, 4), (100, -1, 128, 4), (100, 3, 96, 4), (100, 3, 128, 0)]:
+        assert seg_size(*bad) == -1
+
+
+WS = 1 << 52
+
+
+def call_seg(num_segments=4, workspace=WS, workspace_bytes=None, **kw):
+    kw.setdefault("batch", 1)
+    kw.setdefault("seq_len", 1000)
+    a = chunk_args(**kw)
+    if workspace_bytes is None:
+        workspace_bytes = max(seg_size(a["seq_len"], a["num_heads"], a["head_dim_k"],
+                                       max(num_segments, 1)), 0)
+    return _lib.lib().kda_chunk_fwd_segmented(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"], a["out"],
+        a["final_state"], a["seq_len"], a["num_heads"], a["head_dim_k"], a["head_dim_v"],
+        num_segments, a["dtype"], workspace, workspace_bytes, a["stream"])
+
+
+def test_segmented_valid_call_reaches_the_device_check():
+    assert call_seg() in (DEVICE, OK)
+    assert call_seg(initial_state=None, final_state=None) in (DEVICE, OK)
+
+
+def test_segmented_checks():
+    a = chunk_args()
+    assert call_seg(num_segments=0) == SHAPE
+    assert call_seg(num_segments=-2) == SHAPE
+    assert call_seg(q=None) == NULL
+    assert call_seg(seq_len=-1) == SHAPE
+    assert call_seg(head_dim_k=96, head_dim_v=96) == UNSUP
+    assert call_seg(workspace=None) == NULL
+    assert call_seg(workspace_bytes=seg_size(1000, 3, 128, 4) - 1) == SHAPE
+    assert call_seg(workspace_bytes=-1) == SHAPE
+    assert call_seg(workspace=WS + 128) == ALIGN
+    assert call_seg(workspace=a["out"]) == ALIAS
+    assert call_seg(workspace=a["q"] - 1024) == ALIAS
+    assert call_seg(workspace=a["initial_state"] + 4096) == ALIAS
+
+
+def test_segmented_one_segment_needs_no_workspace():
+    # a single segment (or a sequence of at most one chunk per segment) is the
+    # plain prefill: the workspace is never touched
+    assert call_seg(num_segments=1, workspace=None, workspace_bytes=0) in (DEVICE, OK)
+    assert call_seg(seq_len=32, num_segments=8, workspace=None, workspace_bytes=0) in (DEVICE, OK)
+    assert call_seg(seq_len=0, workspace=None, workspace_bytes=0, q=None, k=None, v=None,
+                    log_alpha=None, beta=None, out=None) in (DEVICE, OK)
+    assert call_seg(num_heads=0, workspace=None, workspace_bytes=0) == OK
 
 
 # ---------------------------------------------------------------- decode_step
