@@ -152,7 +152,9 @@ struct ChunkSrc {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-template <typename T>
+// ZV: zero values (v is not read; its descriptor covers no bytes, so every V
+// load returns zeros).
+template <bool ZV, typename T>
 __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v,
                                               const float *log_alpha, const float *beta,
                                               int64_t tok0, int nvalid, int H, int D,
@@ -164,10 +166,11 @@ __device__ __forceinline__ ChunkSrc chunk_src(const T *q, const T *k, const T *v
                                             kRsrcWord3);
     s.q = __builtin_amdgcn_make_buffer_rsrc((void *)(q + e0), 0, elems * (int)sizeof(T),
                                             kRsrcWord3);
-    // v == NULL reads as zero values: a descriptor covering no bytes
-    s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v ? v + e0 : v), 0,
-                                            v ? elems * (int)sizeof(T) : 0,
-                                            kRsrcWord3);
+    if constexpr (ZV)
+        s.v = __builtin_amdgcn_make_buffer_rsrc((void *)k, 0, 0, kRsrcWord3);
+    else
+        s.v = __builtin_amdgcn_make_buffer_rsrc((void *)(v + e0), 0, elems * (int)sizeof(T),
+                                                kRsrcWord3);
     s.g = scalar_gate ? __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + tok0 * H), 0,
                                                           nvalid * H * 4, kRsrcWord3)
                       : __builtin_amdgcn_make_buffer_rsrc((void *)(log_alpha + e0), 0, elems * 4,
@@ -394,13 +397,20 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
     return acc;
 }
 
-template <typename T, int D, int DVS, bool SG>
+// MODE (compile time, so the output path's code is untouched by it):
+//   kModeOut    the prefill: outputs, final states, snapshots;
+//   kModeState  no outputs (out is not used): final states only;
+//   kModeMap    no outputs, zero values (v is not used) and every workgroup
+//               starting from S = I: the final state is the sequence's state
+//               transition (transposed like every state).
+constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2;
+template <typename T, int D, int DVS, bool SG, int MODE>
 __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
     T *__restrict__ out, float *__restrict__ final_state, float *__restrict__ snapshots,
-    int snap_every, int snap_cap, int init_identity, int num_seqs, int seq_len, int total_tokens,
+    int snap_every, int snap_cap, int num_seqs, int seq_len, int total_tokens,
     int H, int units, int units_per_xcd) {
     typedef Cfg<T, D, DVS, SG> G;
     typedef Mma<T> M;
@@ -464,7 +474,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         const ChunkOffsets<T, D, DVS, SG> offs(wave, lane, h, H, v0);
         auto src = [&](int ci) {
             const int64_t t0 = tbeg + (int64_t)ci * kC;
-            return chunk_src(q, k, v, log_alpha, beta, t0,
+            return chunk_src<MODE == kModeMap>(q, k, v, log_alpha, beta, t0,
                              (int)((tend - t0) < kC ? (tend - t0) : kC), H, D, SG);
         };
         // Two register sets: the loads of chunk n + 2 go out at the start of
@@ -774,7 +784,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     f32x4 Sm[G::NRT];
 #pragma unroll
     for (int t = 0; t < G::NRT; ++t)
-        Sm[t] = init_identity
+        Sm[t] = MODE == kModeMap
                     ? f32x4{vcol == 16 * t + 4 * l4 ? 1.f : 0.f, vcol == 16 * t + 4 * l4 + 1 ? 1.f : 0.f,
                             vcol == 16 * t + 4 * l4 + 2 ? 1.f : 0.f,
                             vcol == 16 * t + 4 * l4 + 3 ? 1.f : 0.f}
@@ -844,11 +854,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 for (int e = 0; e < 4; ++e) r1[e] = b1[e] * X[1][e] - ad[e];
                 Dl[1] = mm16<T>(zero4(), cT3 + 2 * T16, G::LDTT, r1, lane);
             }
-            // O = Q+ S + Mqk Delta (Mqk lower triangular); out == NULL: states only
+            // O = Q+ S + Mqk Delta (Mqk lower triangular); only with outputs
             const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
             const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
 #pragma unroll
-            for (int rt = 0; rt < 2 && out; ++rt) {
+            for (int rt = 0; rt < 2 && MODE == kModeOut; ++rt) {
                 PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 0, lane), Db0);
                 if (sizeof(T) == 4 && rt == 1)
                     PQ[rt] = SM::mma(PQ[rt], SM::a(cMQ + kBS * rt * G::LDT, G::LDT, 1, lane), Db1);
@@ -865,7 +875,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // the chunk's O rows (32 x DVS), whole rows in 16-byte pieces
             constexpr int LV = G::RBV / 16;
 #pragma unroll
-            for (int i = 0; i < G::IO && out; ++i) {
+            for (int i = 0; i < G::IO && MODE == kModeOut; ++i) {
                 const int p = (ct * G::IO + i) * 64 + lane, orow = p / LV, b = 16 * (p % LV);
                 if (orow < nvalid)
                     *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(
@@ -911,46 +921,38 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     }
 }
 
-template <typename T, int D, int DVS, bool SG>
+template <typename T, int D, int DVS, bool SG, int MODE>
 int launch(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
            const float *initial_state, const int32_t *cu_seqlens, void *out, float *final_state,
-           float *snapshots, int snap_every, int snap_cap, int init_identity, int num_seqs,
-           int seq_len, int total_tokens, int H, hipStream_t stream) {
+           float *snapshots, int snap_every, int snap_cap, int num_seqs, int seq_len,
+           int total_tokens, int H, hipStream_t stream) {
     const int64_t units64 = (int64_t)num_seqs * H * (D / DVS);
     if (units64 == 0) return 0;
     if (units64 > (int64_t)1 << 30) return -1;
     const int units = (int)units64;
     const int per_xcd = (units + 7) / 8;
-    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG>), dim3(8 * per_xcd),
+    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE>), dim3(8 * per_xcd),
                        dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
                        initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,
-                       snap_every, snap_cap, init_identity, num_seqs, seq_len, total_tokens, H,
-                       units, per_xcd);
+                       snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <bool SG>
+template <bool SG, int MODE>
 int launch_dtype(const void *q, const void *k, const void *v, const float *log_alpha,
                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                  void *out, float *final_state, float *snapshots, int snapshot_every,
-                 int num_snapshots, int init_identity, int num_seqs, int seq_len,
-                 int total_tokens, int num_heads, int head_dim, int dtype, hipStream_t stream) {
-    if (dtype == kDtypeBf16) {
-        if (head_dim == 128)
-            return launch<bf16, 128, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
-                                             out, final_state, snapshots, snapshot_every,
-                                             num_snapshots, init_identity, num_seqs, seq_len,
-                                             total_tokens, num_heads, stream);
-        return launch<bf16, 64, 64, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                        final_state, snapshots, snapshot_every, num_snapshots,
-                                        init_identity, num_seqs, seq_len, total_tokens, num_heads,
-                                        stream);
-    }
-    return launch<float, 64, 16, SG>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                     final_state, snapshots, snapshot_every, num_snapshots,
-                                     init_identity, num_seqs, seq_len, total_tokens, num_heads,
-                                     stream);
+                 int num_snapshots, int num_seqs, int seq_len, int total_tokens, int num_heads,
+                 int head_dim, int dtype, hipStream_t stream) {
+#define KDA_LAUNCH_ARGS                                                                        \
+    q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state, snapshots,          \
+        snapshot_every, num_snapshots, num_seqs, seq_len, total_tokens, num_heads, stream
+    if (dtype == kDtypeBf16)
+        return head_dim == 128 ? launch<bf16, 128, 64, SG, MODE>(KDA_LAUNCH_ARGS)
+                               : launch<bf16, 64, 64, SG, MODE>(KDA_LAUNCH_ARGS);
+    return launch<float, 64, 16, SG, MODE>(KDA_LAUNCH_ARGS);
+#undef KDA_LAUNCH_ARGS
 }
 
 }  // namespace
@@ -962,15 +964,20 @@ int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *l
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
                      int scalar_gate, int init_identity, hipStream_t stream) {
     if (!snapshots) snapshot_every = kC, num_snapshots = 0;
-    return scalar_gate
-               ? launch_dtype<true>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                    final_state, snapshots, snapshot_every, num_snapshots,
-                                    init_identity, num_seqs, seq_len, total_tokens, num_heads,
-                                    head_dim, dtype, stream)
-               : launch_dtype<false>(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
-                                     final_state, snapshots, snapshot_every, num_snapshots,
-                                     init_identity, num_seqs, seq_len, total_tokens, num_heads,
-                                     head_dim, dtype, stream);
+#define KDA_CHUNK_ARGS                                                                         \
+    q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state, snapshots,          \
+        snapshot_every, num_snapshots, num_seqs, seq_len, total_tokens, num_heads, head_dim,   \
+        dtype, stream
+    if (init_identity) {  // the transition map: no values, no outputs, no snapshots
+        if (v || out || snapshots || initial_state || scalar_gate) return -1;
+        return launch_dtype<false, kModeMap>(KDA_CHUNK_ARGS);
+    }
+    // without outputs (the state-only pass of the segmented prefill): the
+    // channel-gate kernels only
+    if (!out) return scalar_gate ? -1 : launch_dtype<false, kModeState>(KDA_CHUNK_ARGS);
+    return scalar_gate ? launch_dtype<true, kModeOut>(KDA_CHUNK_ARGS)
+                       : launch_dtype<false, kModeOut>(KDA_CHUNK_ARGS);
+#undef KDA_CHUNK_ARGS
 }
 
 }  // namespace kda

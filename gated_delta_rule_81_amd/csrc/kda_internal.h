@@ -22,10 +22,12 @@ int launch_decode_step(const void *q, const void *k, const void *v, const float 
 // multiple of 32) of each sequence is also written, at most num_snapshots
 // entries.  scalar_gate != 0: log_alpha holds one gate per (token, head),
 // [T, H], applied to every key channel (the Gated DeltaNet gate); otherwise
-// [T, H, d_k].  init_identity != 0: every workgroup starts from S = I instead
-// of initial_state (d_k == d_v), which turns the final state into the chunk
-// sequence's state transition when v == NULL (v == NULL reads as zeros).
-// Arguments are already validated.  Returns 0, or -1 if the launch failed.
+// [T, H, d_k].  out == NULL (channel gates only): final states only.
+// init_identity != 0 (then v, out, snapshots and initial_state are NULL and
+// the gates are per channel): every sequence starts from S = I with zero
+// values, so its final state is its state transition (stored transposed).
+// Arguments are already validated.  Returns 0, or -1 if the launch failed or
+// the combination is not one of these.
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                      void *out, float *final_state, float *snapshots, int32_t snapshot_every,
