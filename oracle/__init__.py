@@ -10,6 +10,8 @@ Contents
   * ``kda_snapshots`` -- the same recurrence with the state recorded after
     every N tokens of each sequence.
   * ``gdn_forward`` -- the scalar-gate (Gated DeltaNet) special case.
+  * ``kda_backward`` -- gradients of ``kda_forward`` with respect to every
+    input, token by token in reverse (``kda_oracle.c``).
   * ``forms.projection_forward`` -- a second fp64 witness that builds the
     explicit d_k x d_k transition matrices of the printed KDA update.
   * ``forms.brute_force_exact`` -- exact-rational evaluation through transition
@@ -56,6 +58,10 @@ def open_library(path: str):
         ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp, dp, dp, dp,
         ctypes.c_int]
     lib.kda_oracle_forward.restype = ctypes.c_int
+    lib.kda_oracle_backward.argtypes = [
+        ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64] + [dp] * 14 + [ctypes.c_int]
+    lib.kda_oracle_backward.restype = ctypes.c_int
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -124,6 +130,50 @@ def kda_forward(q, k, v, log_alpha, beta, state0=None, seq_start=None,
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed with code {rc}")
     return out, sT
+
+
+def kda_backward(q, k, v, log_alpha, beta, d_out, d_state=None, state0=None,
+                 seq_start=None, threads: int = 0):
+    """Gradients of ``kda_forward`` in fp64 (``kda_oracle_backward``).
+
+    Inputs as ``kda_forward`` plus d_out [T, H, d_v] (dL/d out) and d_state
+    [N, H, d_v, d_k] (dL/d final state) or None (zero).  Returns a dict of
+    float64 arrays: dq, dk, dlog_alpha [T, H, d_k]; dv [T, H, d_v];
+    dbeta [T, H]; dstate0 [N, H, d_v, d_k] (the initial state's gradient).
+    """
+    q = _f64(q)
+    if q.ndim != 3:
+        raise ValueError("q must be [T, H, d_k]")
+    T, H, dk = q.shape
+    v = _f64(v)
+    if v.ndim != 3 or v.shape[:2] != (T, H):
+        raise ValueError("v must be [T, H, d_v]")
+    dv = v.shape[2]
+    k = _f64(k, (T, H, dk))
+    log_alpha = _f64(log_alpha, (T, H, dk))
+    beta = _f64(beta, (T, H))
+    d_out = _f64(d_out, (T, H, dv))
+    if seq_start is None:
+        seq_start = [0, T]
+    starts = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    N = starts.shape[0] - 1
+    if N < 0 or starts[-1] > T or starts[0] < 0 or np.any(np.diff(starts) < 0):
+        raise ValueError("seq_start must be non-decreasing within [0, T]")
+    s0 = None if state0 is None else _f64(state0, (N, H, dv, dk))
+    ds = None if d_state is None else _f64(d_state, (N, H, dv, dk))
+    g = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+         "dlog_alpha": np.zeros((T, H, dk)), "dbeta": np.zeros((T, H)),
+         "dstate0": np.zeros((N, H, dv, dk))}
+    null = ctypes.POINTER(ctypes.c_double)()
+    rc = _load().kda_oracle_backward(
+        N, starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+        _ptr(s0) if s0 is not None else null, _ptr(d_out),
+        _ptr(ds) if ds is not None else null, _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g["dstate0"]), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
+    return g
 
 
 def kda_forward_dense(q, k, v, log_alpha, beta, state0=None, threads: int = 0):
