@@ -33,6 +33,10 @@ SIGNATURES = {
                                  _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp],
                                 ctypes.c_int),
     "kda_chunk_fwd_segmented_workspace_size": ([_i32, _i32, _i32, _i32], _i64),
+    "kda_chunk_bwd": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _fp,
+                       _fp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp],
+                      ctypes.c_int),
+    "kda_chunk_bwd_workspace_size": ([_i32, _i32, _i32, _i32], _i64),
     "kda_decode_step_scalar_gate": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "kda_decode_step": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp,

@@ -269,6 +269,73 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+int64_t kda_chunk_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t head_dim) {
+    if (total_tokens < 0 || num_seqs < 0 || num_heads < 0 || (head_dim != 64 && head_dim != 128))
+        return -1;
+    return kda::chunk_bwd_workspace_floats(total_tokens, num_seqs, num_heads, head_dim) * 4;
+}
+
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                  float *dlog_alpha, float *dbeta, float *d_initial_state, int32_t batch,
+                  int32_t seq_len, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                  int32_t num_seqs, int32_t dtype, void *workspace, int64_t workspace_bytes,
+                  hipStream_t stream) {
+    if (batch < 0 || seq_len < 0 || num_heads < 0 || head_dim_k <= 0 || head_dim_v <= 0 ||
+        workspace_bytes < 0)
+        return KDA_ERR_SHAPE;
+    if (dtype != kda::kDtypeF32 && dtype != kda::kDtypeBf16) return KDA_ERR_UNSUPPORTED;
+    const bool packed = cu_seqlens != nullptr;
+    if (packed && (batch != 1 || num_seqs < 0)) return KDA_ERR_SHAPE;
+    const int64_t tokens = (int64_t)batch * seq_len;
+    if (tokens > INT32_MAX) return KDA_ERR_SHAPE;
+    const int64_t nseq = packed ? num_seqs : batch;
+    const uint64_t th = (uint64_t)tokens * num_heads;
+    if (th > 0 && (!q || !k || !v || !log_alpha || !beta || !d_out || !dq || !dk || !dv ||
+                   !dlog_alpha || !dbeta))
+        return KDA_ERR_NULL;
+    if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
+    const int d = head_dim_k;
+    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) ||
+        !aligned4(beta) || !aligned16(initial_state) || !aligned4(cu_seqlens) ||
+        !aligned16(d_out) || !aligned16(d_final_state) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv) || !aligned16(dlog_alpha) || !aligned4(dbeta) ||
+        !aligned16(d_initial_state) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const uint64_t need =
+        (uint64_t)kda::chunk_bwd_workspace_floats(tokens, nseq, num_heads, d) * 4;
+    const bool work = nseq > 0 && num_heads > 0;
+    if (work && !workspace) return KDA_ERR_NULL;
+    if (work && (uint64_t)workspace_bytes < need) return KDA_ERR_SHAPE;
+    const uint64_t esz = dtype == kda::kDtypeBf16 ? 2 : 4;
+    const uint64_t sb = (uint64_t)nseq * num_heads * d * d * 4;
+    const Range inputs[] = {{q, th * d * esz}, {k, th * d * esz}, {v, th * d * esz},
+                            {log_alpha, th * d * 4}, {beta, th * 4}, {initial_state, sb},
+                            {cu_seqlens, packed ? (uint64_t)(nseq + 1) * 4 : 0},
+                            {d_out, th * d * esz}, {d_final_state, sb}};
+    const Range outputs[] = {{dq, th * d * esz}, {dk, th * d * esz}, {dv, th * d * esz},
+                             {dlog_alpha, th * d * 4}, {dbeta, th * 4}, {d_initial_state, sb},
+                             {workspace, work ? need : 0}};
+    for (int i = 0; i < 7; ++i) {
+        for (const Range &r : inputs)
+            if (overlap(outputs[i], r)) return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outputs[i], outputs[j])) return KDA_ERR_ALIAS;
+    }
+    if (!work) return KDA_OK;
+    const int st = check_device();
+    if (st != KDA_OK) return st;
+    const int rc = kda::launch_chunk_bwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
+                                         d_out, d_final_state, dq, dk, dv, dlog_alpha, dbeta,
+                                         d_initial_state, static_cast<float *>(workspace),
+                                         (int32_t)nseq, seq_len, (int32_t)tokens, num_heads, d,
+                                         dtype, stream);
+    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                   void *out, float *final_state, int32_t batch, int32_t seq_len,

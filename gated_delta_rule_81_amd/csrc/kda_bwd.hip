@@ -1,0 +1,500 @@
+// kda_bwd.hip -- chunked backward of the KDA forward pass (gradients of the
+// outputs and the final state with respect to q, k, v, log_alpha, beta and
+// the initial state), fp32 arithmetic on the matrix cores.
+//
+// Pages cited (by title):
+//   [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (§四: the KDA
+//                   update; §六.2: a chunk's updates as matrix products).
+//   [Kimi-Linear]   "Kimi Linear 最多砍掉 75% KV Cache：全注意力真要退场了吗？"
+//                   (ai.concitech.org), the section on KDA's per-channel
+//                   forgetting: the chunkwise kernel exists so that training
+//                   runs as matrix products.
+//
+// The pages give no gradient; this is the reverse-mode derivative of the
+// chunk form of the forward, per chunk of C = 16 tokens with entering state
+// S0 (d_k x d_v) and Gamma = the within-chunk prefix of log_alpha:
+//   K+ = K e^G, K- = K e^-G, Q+ = Q e^G, Ke = K e^(G_last - G), gam = e^G_last,
+//   A = StrictTril(diag(b) K+ K-^T), M = Tril(Q+ K-^T), T = (I + A)^-1,
+//   X = V - K+ S0,  Delta = T diag(b) X,
+//   O = Q+ S0 + M Delta,  S_C = diag(gam) S0 + Ke^T Delta.
+// Given dO and dS_C:
+//   dDelta = M^T dO + Ke dS_C,  lam = T^T dDelta,  dX = dV = diag(b) lam,
+//   dA = -StrictTril(lam Delta^T),  P = diag(b) dA,  dM = Tril(dO Delta^T),
+//   db = rowsum(X * lam) + rowsum(dA * K+K-^T),
+//   dQ+ = dO S0^T + dM K-,  dK+ = -dX S0^T + P K-,  dK- = dM^T Q+ + P^T K+,
+//   dKe = Delta dS_C^T,  dS0 = diag(gam) dS_C + Q+^T dO - K+^T dX,
+//   dG_last = gam * rowsum(S0 * dS_C) + colsum(dKe * Ke),
+//   dQ = dQ+ e^G,  dK = dK+ e^G + dK- e^-G + dKe e^(G_last - G),
+//   dG = dQ+ Q+ + dK+ K+ - dK- K- - dKe Ke  (+ dG_last on the last row),
+//   dlog_alpha = the within-chunk suffix sum of dG.
+// A ragged last chunk is padded with zero rows (and zero gates), which add
+// nothing.  16-token chunks keep e^(+-G) within fp32 under the library's
+// numerics contract (a 16-token gate sum above -80).
+//
+// One workgroup per (sequence, head), D / 16 waves.  Pass 1 runs the chunks
+// forward and writes each chunk's entering state to the workspace; pass 2 runs
+// them backward.  The states live in registers in two orientations: wave w
+// owns value columns 16w.. of S (for products that contract over d_k) and key
+// columns 16w.. of M = S^T (for products that contract over d_v), so no
+// product needs a cross-wave reduction.  Chunk operands are staged in LDS as
+// fp32.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kBC = 16;  // tokens per chunk of the backward
+
+template <int D>
+struct BwdCfg {
+    static constexpr int W = D / 16;  // waves; also 16-wide tiles along d
+    static constexpr int THREADS = 64 * W;
+    static constexpr int LD = D + 4;   // row stride of [16][D] arrays (floats)
+    static constexpr int LS = 20;      // row stride of 16 x 16 arrays (16-byte rows)
+    static constexpr int ROW = kBC * LD;
+    static constexpr int SQ = kBC * LS;
+    static constexpr int oQp = 0, oKp = ROW, oKm = 2 * ROW, oKe = 3 * ROW, oG = 4 * ROW,
+                         oV = 5 * ROW, oDO = 6 * ROW, oDl = 7 * ROW, oLm = 8 * ROW,
+                         oDX = 9 * ROW;
+    static constexpr int oBr = 10 * ROW, oA = oBr + SQ, oM = oA + SQ, oT = oM + SQ,
+                         oTt = oT + SQ, oP = oTt + SQ, oDM = oP + SQ;
+    static constexpr int oGam = oDM + SQ, oBeta = oGam + D, oDB = oBeta + kBC;
+    static constexpr int FLOATS = oDB + (W + 1) * kBC;
+};
+
+__device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The products below follow one lane contract (v_mfma_f32_16x16x4f32): lane
+// l supplies row i = l % 16 of A and column j = l % 16 of B for contraction
+// indices chosen by g = l / 16, and holds output rows 4g + e (e = 0..3) of
+// column l % 16.  The contraction index of step e within a 16-block is
+// 4g + e, identical on both operands.
+
+// A row-major in LDS (A[i][kk]), B from registers: B[t][e] = B[kk = 16t+4g+e][j].
+template <int NT>
+__device__ __forceinline__ f32x4 mm_lds_reg(f32x4 acc, const float *A, int lda,
+                                            const f32x4 (&B)[NT], int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mf(a[e], B[t][e], acc);
+    }
+    return acc;
+}
+
+// A row-major 16 x 16 in LDS, B a register tile: B[e] = B[kk = 4g+e][j].
+__device__ __forceinline__ f32x4 mm_lds_tile(f32x4 acc, const float *A, int lda, const f32x4 &B,
+                                             int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mf(a[e], B[e], acc);
+    return acc;
+}
+
+// A row-major in LDS, B given by rows of Bt (Bt[j][kk]), contraction K.
+template <int K>
+__device__ __forceinline__ f32x4 mm_lds_ldst(f32x4 acc, const float *A, int lda, const float *Bt,
+                                             int ldb, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int kb = 0; kb < K / 16; ++kb) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 16 * kb + 4 * g);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(Bt + r * ldb + 16 * kb + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mf(a[e], b[e], acc);
+    }
+    return acc;
+}
+
+// A given transposed (A[i][kk] = At[kk][i]), B row-major (Bm[kk][j]), contraction 16.
+__device__ __forceinline__ f32x4 mm_ldst_lds(f32x4 acc, const float *At, int lda, const float *Bm,
+                                             int ldb, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        acc = mf(At[(4 * g + e) * lda + r], Bm[(4 * g + e) * ldb + r], acc);
+    return acc;
+}
+
+// A row-major 16 x 16 in LDS, B row-major (Bm[kk][j]), contraction 16.
+__device__ __forceinline__ f32x4 mm_lds_lds(f32x4 acc, const float *A, int lda, const float *Bm,
+                                            int ldb, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mf(a[e], Bm[(4 * g + e) * ldb + r], acc);
+    return acc;
+}
+
+// A given transposed (A[i][kk] = At[kk][i]), B a register tile, contraction 16.
+__device__ __forceinline__ f32x4 mm_ldst_tile(f32x4 acc, const float *At, int lda,
+                                              const f32x4 &B, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mf(At[(4 * g + e) * lda + r], B[e], acc);
+    return acc;
+}
+
+// Keeps the scheduler from hoisting the LDS reads of later products above
+// this point (which would hold their operands in registers early).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
+// Sum over the 16 lanes of a row group (lanes with equal l / 16).
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ log_alpha, const float *__restrict__ beta,
+    const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
+    const T *__restrict__ d_out, const float *__restrict__ d_final, T *__restrict__ dq,
+    T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dlog_alpha,
+    float *__restrict__ dbeta, float *__restrict__ d_initial, float *__restrict__ ckpt,
+    int seq_len, int total_tokens, int H) {
+    typedef BwdCfg<D> G;
+    constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
+    __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
+    float *sQp = sm + G::oQp, *sKp = sm + G::oKp, *sKm = sm + G::oKm, *sKe = sm + G::oKe;
+    float *sG = sm + G::oG, *sV = sm + G::oV, *sDO = sm + G::oDO, *sDl = sm + G::oDl;
+    float *sLm = sm + G::oLm, *sDX = sm + G::oDX, *sBr = sm + G::oBr, *sA = sm + G::oA;
+    float *sM = sm + G::oM, *sT = sm + G::oT, *sTt = sm + G::oTt, *sP = sm + G::oP;
+    float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    int64_t tbeg, tend;
+    if (cu_seqlens) {
+        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+        b = b < a ? a : (b > total_tokens ? total_tokens : b);
+        tbeg = a, tend = b;
+    } else {
+        tbeg = (int64_t)n * seq_len, tend = tbeg + seq_len;
+    }
+    const int nch = (int)((tend - tbeg + kBC - 1) / kBC);
+    const int64_t DD = (int64_t)D * D;
+    // chunk c of this sequence keeps its entering state in slot tbeg / 16 + n + c
+    float *ck = ckpt + ((tbeg / kBC + n) * H + h) * DD;
+    const int64_t ck_stride = (int64_t)H * DD;
+    const int64_t sbase = ((int64_t)n * H + h) * DD;
+    const int vcol = 16 * w + r;  // S orientation: this lane's value column
+    const int kcol = 16 * w + r;  // M orientation: this lane's key column
+
+    // Stage chunk c: raw rows as fp32, the prefix G, K+, K-, Q+, Ke, gam, the
+    // 16 x 16 matrices K+K-^T, A, M and T = (I + A)^-1 (and T^T).
+    auto prep = [&](int c, bool with_grad) -> int {
+        const int64_t t0 = tbeg + (int64_t)c * kBC;
+        const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
+        for (int idx = tid; idx < kBC * D; idx += G::THREADS) {
+            const int tok = idx / D, ch = idx % D;
+            const bool ok = tok < nval;
+            const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
+            sQp[tok * LD + ch] = ok ? to_f32(q[gi]) : 0.f;
+            sKp[tok * LD + ch] = ok ? to_f32(k[gi]) : 0.f;
+            sV[tok * LD + ch] = ok ? to_f32(v[gi]) : 0.f;
+            sG[tok * LD + ch] = ok ? log_alpha[gi] : 0.f;
+            if (with_grad) sDO[tok * LD + ch] = ok ? to_f32(d_out[gi]) : 0.f;
+        }
+        if (tid < kBC) sBeta[tid] = tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
+        __syncthreads();
+        if (tid < D) {
+            const int ch = tid;
+            float acc = 0.f;
+#pragma unroll
+            for (int tok = 0; tok < kBC; ++tok) {
+                acc += sG[tok * LD + ch];
+                sG[tok * LD + ch] = acc;
+            }
+            const float gl = acc;
+            sGam[ch] = __expf(gl);
+#pragma unroll
+            for (int tok = 0; tok < kBC; ++tok) {
+                const float gm = sG[tok * LD + ch], eg = __expf(gm);
+                const float kr = sKp[tok * LD + ch];
+                sKp[tok * LD + ch] = kr * eg;
+                sKm[tok * LD + ch] = kr / eg;
+                sKe[tok * LD + ch] = kr * __expf(gl - gm);
+                sQp[tok * LD + ch] *= eg;
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+            const f32x4 b = mm_lds_ldst<D>(zero4(), sKp, LD, sKm, LD, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g4 + e;
+                sBr[i * LS + r] = b[e];
+                sA[i * LS + r] = r < i ? sBeta[i] * b[e] : 0.f;
+            }
+        } else if (w == 1) {
+            const f32x4 m = mm_lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g4 + e;
+                sM[i * LS + r] = r <= i ? m[e] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (w == 0 && lane < kBC) {  // column j = lane of T by forward substitution
+            const int j = lane;
+            float col[kBC];
+#pragma unroll
+            for (int i = 0; i < kBC; ++i) {
+                float s = i == j ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) s -= sA[i * LS + m] * col[m];
+                col[i] = s;
+                sT[i * LS + j] = s;
+                sTt[j * LS + i] = s;
+                sched_fence();
+            }
+        }
+        __syncthreads();
+        return nval;
+    };
+
+    // ------------------------------------------------------------ pass 1
+    f32x4 Ss[NT];  // S0 of the chunk: [k = 16t + 4g + e][v = vcol]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        Ss[t] = initial_state ? *reinterpret_cast<const f32x4 *>(
+                                    initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * g4)
+                              : zero4();
+    for (int c = 0; c < nch; ++c) {
+        prep(c, false);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4 *>(ck + c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4) =
+                Ss[t];
+        const f32x4 pk = mm_lds_reg(zero4(), sKp, LD, Ss, lane);
+        f32x4 xb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 4 * g4 + e;
+            xb[e] = sBeta[tok] * (sV[tok * LD + vcol] - pk[e]);
+        }
+        const f32x4 dl = mm_lds_tile(zero4(), sT, LS, xb, lane);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 u = mm_ldst_tile(zero4(), sKe + 16 * t, LD, dl, lane);
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ss[t][e] = gm[e] * Ss[t][e] + u[e];
+            sched_fence();
+        }
+        __syncthreads();
+    }
+
+    // ------------------------------------------------------------ pass 2
+    f32x4 dSs[NT];  // dL/dS at the chunk end, S orientation (value column vcol)
+    f32x4 dMm[NT];  // the same in M orientation: [v = 16j + 4g + e][k = kcol]
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        dSs[t] = d_final ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vcol * D +
+                                                            16 * t + 4 * g4)
+                         : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dMm[t][e] = d_final ? d_final[sbase + (int64_t)(16 * t + 4 * g4 + e) * D + kcol] : 0.f;
+    }
+    for (int c = nch - 1; c >= 0; --c) {
+        const int nval = prep(c, true);
+        const int64_t t0 = tbeg + (int64_t)c * kBC;
+        const float *S0 = ck + c * ck_stride;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            Ss[t] = *reinterpret_cast<const f32x4 *>(S0 + (int64_t)vcol * D + 16 * t + 4 * g4);
+        // value-column products (this wave's 16 columns of X, Delta, lam, dX)
+        const f32x4 pk = mm_lds_reg(zero4(), sKp, LD, Ss, lane);
+        f32x4 x, xb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 4 * g4 + e;
+            x[e] = sV[tok * LD + vcol] - pk[e];
+            xb[e] = sBeta[tok] * x[e];
+        }
+        const f32x4 dl = mm_lds_tile(zero4(), sT, LS, xb, lane);
+        sched_fence();
+        f32x4 ddl = mm_ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
+        ddl = mm_lds_reg(ddl, sKe, LD, dSs, lane);
+        sched_fence();
+        const f32x4 lam = mm_lds_tile(zero4(), sTt, LS, ddl, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 4 * g4 + e;
+            const float dx = sBeta[tok] * lam[e];
+            sDl[tok * LD + vcol] = dl[e];
+            sLm[tok * LD + vcol] = lam[e];
+            sDX[tok * LD + vcol] = dx;
+            if (tok < nval) dv[((t0 + tok) * H + h) * (int64_t)D + vcol] = from_f32<T>(dx);
+            const float pb = row16_sum(x[e] * lam[e]);
+            if (r == 0) sDB[w * kBC + tok] = pb;
+        }
+        __syncthreads();
+        if (w == 0) {  // dA, P = diag(b) dA and the K+K-^T part of db
+            const f32x4 ld = mm_lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g4 + e;
+                const float da = r < i ? -ld[e] : 0.f;
+                sP[i * LS + r] = sBeta[i] * da;
+                const float pb = row16_sum(da * sBr[i * LS + r]);
+                if (r == 0) sDB[G::W * kBC + i] = pb;
+            }
+        } else if (w == 1) {  // dM = Tril(dO Delta^T)
+            const f32x4 od = mm_lds_ldst<D>(zero4(), sDO, LD, sDl, LD, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * g4 + e;
+                sDM[i * LS + r] = r <= i ? od[e] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (tid < nval) {
+            float s = 0.f;
+#pragma unroll
+            for (int ww = 0; ww <= G::W; ++ww) s += sDB[ww * kBC + tid];
+            dbeta[(t0 + tid) * H + h] = s;
+        }
+        // key-column products (this wave's 16 key columns), with S0 in M orientation
+        f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sm[t][e] = S0[(int64_t)(16 * t + 4 * g4 + e) * D + kcol];
+        const f32x4 dqp = mm_lds_lds(mm_lds_reg(zero4(), sDO, LD, Sm, lane), sDM, LS, sKm + 16 * w,
+                                     LD, lane);
+        sched_fence();
+        const f32x4 xs = mm_lds_reg(zero4(), sDX, LD, Sm, lane);
+        sched_fence();
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s1 += Sm[t][e] * dMm[t][e];
+        const f32x4 pkm = mm_lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
+        const f32x4 dkm = mm_ldst_lds(mm_ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
+                                      LS, sKp + 16 * w, LD, lane);
+        sched_fence();
+        const f32x4 dke = mm_lds_reg(zero4(), sDl, LD, dMm, lane);
+        sched_fence();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s2 += dke[e] * sKe[(4 * g4 + e) * LD + kcol];
+        s1 += __shfl_xor(s1, 16, 64);
+        s1 += __shfl_xor(s1, 32, 64);
+        s2 += __shfl_xor(s2, 16, 64);
+        s2 += __shfl_xor(s2, 32, 64);
+        const float gamk = sGam[kcol];
+        const float gl = sG[(kBC - 1) * LD + kcol];
+        float dgm[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 4 * g4 + e;
+            const float gm = sG[tok * LD + kcol], eg = __expf(gm);
+            const float dkp = pkm[e] - xs[e];
+            const float qv = dqp[e] * eg;
+            const float kv = dkp * eg + dkm[e] / eg + dke[e] * __expf(gl - gm);
+            dgm[e] = dqp[e] * sQp[tok * LD + kcol] + dkp * sKp[tok * LD + kcol] -
+                     dkm[e] * sKm[tok * LD + kcol] - dke[e] * sKe[tok * LD + kcol];
+            if (tok < nval) {
+                const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + kcol;
+                dq[gi] = from_f32<T>(qv);
+                dk[gi] = from_f32<T>(kv);
+            }
+        }
+        if (g4 == 3) dgm[3] += gamk * s1 + s2;  // G_last enters through the last row
+        // suffix sums over the 16 rows: within the lane, then over the groups above
+        dgm[2] += dgm[3];
+        dgm[1] += dgm[2];
+        dgm[0] += dgm[1];
+        float above = 0.f;
+#pragma unroll
+        for (int gg = 1; gg < 4; ++gg) {
+            const float tot = __shfl(dgm[0], r + 16 * gg, 64);
+            if (gg > g4) above += tot;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tok = 4 * g4 + e;
+            if (tok < nval)
+                dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] = dgm[e] + above;
+        }
+        // state gradient before the chunk, both orientations
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 u = mm_ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
+            const f32x4 y = mm_ldst_lds(zero4(), sKp + 16 * t, LD, sDX + 16 * w, LD, lane);
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
+            const f32x4 um = mm_ldst_lds(zero4(), sDO + 16 * t, LD, sQp + 16 * w, LD, lane);
+            const f32x4 ym = mm_ldst_lds(zero4(), sDX + 16 * t, LD, sKp + 16 * w, LD, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dMm[t][e] = gamk * dMm[t][e] + um[e] - ym[e];
+            sched_fence();
+        }
+        __syncthreads();
+    }
+    if (d_initial) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4 *>(d_initial + sbase + (int64_t)vcol * D + 16 * t + 4 * g4) =
+                dSs[t];
+    }
+}
+
+template <typename T, int D>
+int launch_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+               const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+               const void *d_out, const float *d_final, void *dq, void *dk, void *dv,
+               float *dlog_alpha, float *dbeta, float *d_initial, float *ckpt, int num_seqs,
+               int seq_len, int total_tokens, int H, hipStream_t stream) {
+    const int64_t units = (int64_t)num_seqs * H;
+    if (units == 0) return 0;
+    if (units > (int64_t)1 << 30) return -1;
+    hipLaunchKernelGGL((chunk_bwd_kernel<T, D>), dim3((unsigned)units),
+                       dim3(BwdCfg<D>::THREADS), 0, stream, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
+                       initial_state, cu_seqlens, static_cast<const T *>(d_out), d_final,
+                       static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv),
+                       dlog_alpha, dbeta, d_initial, ckpt, seq_len, total_tokens, H);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace
+
+int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
+                                   int head_dim) {
+    return (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim;
+}
+
+int launch_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                     const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                     float *dlog_alpha, float *dbeta, float *d_initial_state, float *workspace,
+                     int32_t num_seqs, int32_t seq_len, int32_t total_tokens, int32_t num_heads,
+                     int head_dim, int dtype, hipStream_t stream) {
+#define KDA_BWD_ARGS                                                                           \
+    q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_out, d_final_state, dq, dk, dv,     \
+        dlog_alpha, dbeta, d_initial_state, workspace, num_seqs, seq_len, total_tokens,        \
+        num_heads, stream
+    if (dtype == kDtypeBf16)
+        return head_dim == 128 ? launch_bwd<bf16, 128>(KDA_BWD_ARGS)
+                               : launch_bwd<bf16, 64>(KDA_BWD_ARGS);
+    return head_dim == 128 ? launch_bwd<float, 128>(KDA_BWD_ARGS)
+                           : launch_bwd<float, 64>(KDA_BWD_ARGS);
+#undef KDA_BWD_ARGS
+}
+
+}  // namespace kda

@@ -49,4 +49,20 @@ int launch_segment_bounds(int32_t *cu, int nseg, int seg_len, int total, hipStre
 int launch_segment_fold(const float *m0, const float *X, const float *Y, float *m_in, int nseg,
                         int H, int head_dim, hipStream_t stream);
 
+// Chunked backward: gradients of the prefill's outputs and final states with
+// respect to q, k, v, log_alpha, beta and the initial states.  Sequences as
+// for launch_chunk_fwd (dense when cu_seqlens == NULL).  d_final_state,
+// initial_state and d_initial_state may be NULL (zero / not written).  The
+// workspace holds chunk_bwd_workspace_floats(...) fp32 values (the entering
+// state of every 16-token chunk).  Arguments are already validated.  Returns
+// 0, or -1 if the launch failed.
+int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
+                                   int head_dim);
+int launch_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                     const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                     float *dlog_alpha, float *dbeta, float *d_initial_state, float *workspace,
+                     int32_t num_seqs, int32_t seq_len, int32_t total_tokens, int32_t num_heads,
+                     int head_dim, int dtype, hipStream_t stream);
+
 }  // namespace kda

@@ -219,6 +219,77 @@ def chunk_fwd_segmented(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, final_state
 
 
+def bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int) -> int:
+    """Bytes of workspace ``chunk_bwd`` needs (``kda_chunk_bwd_workspace_size``)."""
+    n = lib().kda_chunk_bwd_workspace_size(total_tokens, num_seqs, num_heads, head_dim)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
+              beta: torch.Tensor, d_out: torch.Tensor,
+              d_final_state: Optional[torch.Tensor] = None,
+              initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, *,
+              workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None,
+              output_initial_state_grad: bool = True) -> dict:
+    """Gradients of ``chunk_fwd`` (``kda_chunk_bwd``): given dL/d out and
+    dL/d final_state (None = zero), returns a dict with dq, dk, dv (dtype of
+    q), dlog_alpha, dbeta (fp32) and d_initial_state (fp32, or None when
+    ``output_initial_state_grad`` is False).  Inputs as for ``chunk_fwd``;
+    ``grads`` may hold preallocated outputs under the same names, and
+    ``workspace`` a uint8 device tensor of ``bwd_workspace_size`` bytes.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for t, name, dt, shp in ((q, "q", q.dtype, (B, T, H, dk)), (k, "k", q.dtype, (B, T, H, dk)),
+                             (v, "v", q.dtype, (B, T, H, dv)),
+                             (log_alpha, "log_alpha", torch.float32, (B, T, H, dk)),
+                             (beta, "beta", torch.float32, (B, T, H)),
+                             (d_out, "d_out", q.dtype, (B, T, H, dv))):
+        _expect(t, name, dt, shp, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be 1-D")
+        _expect(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    _expect(initial_state, "initial_state", torch.float32, (N, H, dv, dk), dev)
+    _expect(d_final_state, "d_final_state", torch.float32, (N, H, dv, dk), dev)
+    g = dict(grads or {})
+    shapes = {"dq": (q.dtype, (B, T, H, dk)), "dk": (q.dtype, (B, T, H, dk)),
+              "dv": (q.dtype, (B, T, H, dv)), "dlog_alpha": (torch.float32, (B, T, H, dk)),
+              "dbeta": (torch.float32, (B, T, H)),
+              "d_initial_state": (torch.float32, (N, H, dv, dk))}
+    for name, (dt, shp) in shapes.items():
+        if name == "d_initial_state" and not output_initial_state_grad and name not in g:
+            g[name] = None
+            continue
+        if g.get(name) is None:
+            g[name] = torch.empty(shp, dtype=dt, device=dev)
+        _expect(g[name], name, dt, shp, dev)
+    need = bwd_workspace_size(B * T, N, H, dk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _expect(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), _ptr(d_out), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g["d_initial_state"]),
+        B, T, H, dk, dv, N if cu_seqlens is not None else 0, _DTYPES[q.dtype],
+        _ptr(workspace), workspace.numel(), stream)
+    check(rc, "kda_chunk_bwd")
+    return g
+
+
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, log_alpha: torch.Tensor,
                 beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None,
                 scalar_gate: bool = False) -> torch.Tensor:

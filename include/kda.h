@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -216,6 +216,50 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
  */
 int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_heads,
                                                int32_t head_dim, int32_t num_segments);
+
+/*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd: given dL/d out and dL/d
+ * final_state, the gradients with respect to q, k, v, log_alpha, beta and
+ * initial_state, for training.  The pages give training as the reason for the
+ * chunkwise form ([Kimi-Linear], the section on KDA's per-channel forgetting:
+ * training runs as matrix products instead of a token-serial RNN) but state
+ * no gradient; this is the exact derivative of the recurrence of kda_chunk_fwd
+ * (up to rounding), computed chunk by chunk (16 tokens) in reverse with each
+ * chunk's entering state recomputed by a forward pass in the same call.
+ *
+ * Inputs: q, k, v, log_alpha, beta, initial_state, cu_seqlens, batch, seq_len,
+ * num_heads, head_dim_k, head_dim_v, num_seqs and dtype exactly as given to
+ * kda_chunk_fwd (same layouts and rules; initial_state may be NULL = zeros), and
+ *   d_out          [B, T, H, d_v] dtype: dL/d out.
+ *   d_final_state  [N, H, d_v, d_k] fp32 (stored transposed like every
+ *                  state), or NULL for zero.
+ * Outputs (caller-owned, written completely for every token of every sequence):
+ *   dq, dk         [B, T, H, d_k] dtype;  dv [B, T, H, d_v] dtype;
+ *   dlog_alpha     [B, T, H, d_k] fp32;   dbeta [B, T, H] fp32 (4-byte aligned);
+ *   d_initial_state [N, H, d_v, d_k] fp32, or NULL (not written).
+ * workspace: caller-owned device scratch, 16-byte aligned, of at least
+ * kda_chunk_bwd_workspace_size(B * T, N, H, d_k) bytes (else KDA_ERR_SHAPE;
+ * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state; contents
+ * on return are unspecified.  No output may overlap an input, another output or
+ * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
+ * bf16 (fp32 arithmetic inside for both).  Same numerics contract as
+ * kda_chunk_fwd.  Returns KDA_OK or a kda_status error code.
+ */
+int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
+                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                  const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                  float *dlog_alpha, float *dbeta, float *d_initial_state, int32_t batch,
+                  int32_t seq_len, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                  int32_t num_seqs, int32_t dtype, void *workspace, int64_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Bytes of workspace kda_chunk_bwd needs for total_tokens = B * T tokens in
+ * num_seqs sequences: (total_tokens / 16 + num_seqs + 1) * num_heads *
+ * head_dim^2 * 4.  -1 for negative sizes or head_dim not 64/128.  Host only.
+ */
+int64_t kda_chunk_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs, int32_t num_heads,
+                                     int32_t head_dim);
 
 /*
  * kda_decode_step -- one new token per session against a stored state: the

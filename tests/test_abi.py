@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["kda_abi_version", "kda_chunk_fwd", "kda_chunk_fwd_scalar_gate",
+        ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
+         "kda_chunk_fwd", "kda_chunk_fwd_scalar_gate",
          "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_size",
          "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_scalar_gate",
          "kda_status_string"])
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 4
+    assert L.kda_abi_version() == 5
     for code in range(-7, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
@@ -293,6 +294,68 @@ def test_segmented_one_segment_needs_no_workspace():
     assert call_seg(seq_len=0, workspace=None, workspace_bytes=0, q=None, k=None, v=None,
                     log_alpha=None, beta=None, out=None) in (DEVICE, OK)
     assert call_seg(num_heads=0, workspace=None, workspace_bytes=0) == OK
+
+
+# ---------------------------------------------------------------- chunk_bwd
+def test_bwd_workspace_size():
+    f = _lib.lib().kda_chunk_bwd_workspace_size
+    assert f(200, 2, 3, 128) == (200 // 16 + 2 + 1) * 3 * 128 * 128 * 4
+    assert f(0, 0, 3, 64) == 1 * 3 * 64 * 64 * 4
+    for bad in [(-1, 1, 1, 64), (10, -1, 1, 64), (10, 1, -1, 64), (10, 1, 1, 96)]:
+        assert f(*bad) == -1
+
+
+def call_bwd(workspace="auto", workspace_bytes=None, **kw):
+    b = Buf()
+    b.next = 1 << 47  # clear of the buffers chunk_args hands out
+    grads = dict(d_out=b(), d_final_state=b(), dq=b(), dk=b(), dv=b(), dlog_alpha=b(),
+                 dbeta=b(), d_initial_state=b())
+    for key in list(grads):
+        if key in kw:
+            grads[key] = kw.pop(key)
+    a = chunk_args(**kw)
+    N = a["num_seqs"] if a["cu_seqlens"] else a["batch"]
+    if workspace == "auto":
+        workspace = 1 << 52
+    if workspace_bytes is None:
+        workspace_bytes = max(0, _lib.lib().kda_chunk_bwd_workspace_size(
+            a["batch"] * a["seq_len"], N, a["num_heads"], a["head_dim_k"]))
+    return _lib.lib().kda_chunk_bwd(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"], a["cu_seqlens"],
+        grads["d_out"], grads["d_final_state"], grads["dq"], grads["dk"], grads["dv"],
+        grads["dlog_alpha"], grads["dbeta"], grads["d_initial_state"], a["batch"], a["seq_len"],
+        a["num_heads"], a["head_dim_k"], a["head_dim_v"], a["num_seqs"], a["dtype"], workspace,
+        workspace_bytes, a["stream"])
+
+
+def test_bwd_valid_call_reaches_the_device_check():
+    assert call_bwd() in (DEVICE, OK)
+    assert call_bwd(initial_state=None, d_final_state=None, d_initial_state=None) in (DEVICE, OK)
+    assert call_bwd(dtype=F32) in (DEVICE, OK)  # fp32 at d = 128 is supported here
+
+
+@pytest.mark.parametrize("name", ["d_out", "dq", "dk", "dv", "dlog_alpha", "dbeta"])
+def test_bwd_null_required(name):
+    assert call_bwd(**{name: None}) == NULL
+
+
+def test_bwd_checks():
+    a = chunk_args()
+    assert call_bwd(workspace=None) == NULL
+    assert call_bwd(workspace_bytes=1024) == SHAPE
+    assert call_bwd(workspace_bytes=-1) == SHAPE
+    assert call_bwd(workspace=(1 << 52) + 8) == ALIGN
+    assert call_bwd(dbeta=(1 << 51) + 4) in (DEVICE, OK)  # 4-byte alignment suffices
+    assert call_bwd(dq=(1 << 51) + 4) == ALIGN
+    assert call_bwd(head_dim_k=96, head_dim_v=96) == UNSUP
+    assert call_bwd(head_dim_v=64) == UNSUP
+    assert call_bwd(batch=-1) == SHAPE
+    assert call_bwd(dq=a["q"]) == ALIAS
+    assert call_bwd(workspace=a["k"]) == ALIAS
+    same = (1 << 49)
+    assert call_bwd(dq=same, dk=same) == ALIAS
+    assert call_bwd(batch=0, workspace=None) == OK
+    assert call_bwd(num_heads=0, workspace=None) == OK
 
 
 # ---------------------------------------------------------------- decode_step

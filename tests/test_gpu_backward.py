@@ -1,0 +1,167 @@
+"""GPU parity of kda_chunk_bwd (gradients of the prefill) against the fp64
+backward oracle, through the C ABI.
+
+``oracle.kda_backward`` is the token-by-token reverse-mode derivative of the
+recurrence, pinned on the CPU by finite differences of the forward oracle
+(tests/test_oracle_backward.py).  Every gradient is compared per (sequence,
+head) slice with the max-relative-L2 metric of the forward tests; the bounds
+are the forward's: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.  The loss
+gradients d_out ~ N(0, 1) and d_final_state ~ N(0, 0.1^2) are seeded draws.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import TOL, f64, max_rel_l2, say, seq_starts
+
+import gated_delta_rule_81_amd as kda
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GRADS = ("dq", "dk", "dv", "dlog_alpha", "dbeta")
+
+
+def loss_grads(inp, seed):
+    q = inp["q"]
+    B, T, H, D = q.shape
+    N = len(seq_starts(inp)) - 1
+    gen = torch.Generator().manual_seed(seed)
+    d_out = torch.randn(B, T, H, D, generator=gen).to(q.dtype)
+    d_fin = torch.randn(N, H, D, D, generator=gen) * 0.1
+    return d_out, d_fin
+
+
+def run_gpu(inp, d_out, d_fin, **kw):
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d_out.to(DEV),
+                      None if d_fin is None else d_fin.to(DEV), d["initial_state"],
+                      d.get("cu_seqlens"), **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def oracle_grads(inp, d_out, d_fin, heads=None, threads=0):
+    q = inp["q"]
+    B, T, H, D = q.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    flat = lambda x: f64(x.reshape(B * T, *x.shape[2:]))[:, heads]
+    s0 = inp.get("initial_state")
+    return oracle.kda_backward(
+        flat(q), flat(inp["k"]), flat(inp["v"]), flat(inp["log_alpha"]), flat(inp["beta"]),
+        flat(d_out), d_state=None if d_fin is None else f64(d_fin)[:, heads],
+        state0=None if s0 is None else f64(s0)[:, heads], seq_start=seq_starts(inp),
+        threads=threads)
+
+
+def compare(inp, g, ref, heads=None, label=""):
+    q = inp["q"]
+    B, T, H, D = q.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    st = seq_starts(inp)
+    errs = {}
+    for name in GRADS:
+        got = f64(g[name].reshape(B * T, *g[name].shape[2:]))
+        pairs = [(got[st[n]:st[n + 1], h], ref[name][st[n]:st[n + 1], j])
+                 for n in range(len(st) - 1) for j, h in enumerate(heads) if st[n + 1] > st[n]]
+        errs[name] = max_rel_l2(pairs) if pairs else 0.0
+    if g["d_initial_state"] is not None:
+        got = f64(g["d_initial_state"])
+        errs["d_initial_state"] = max_rel_l2([(got[n, h], ref["dstate0"][n, j])
+                                              for n in range(len(st) - 1)
+                                              for j, h in enumerate(heads)])
+    tol = TOL[q.dtype]
+    print(f"{label}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f" (tol {tol})")
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+
+
+@pytest.mark.parametrize("T", [1, 16, 40, 129])
+def test_bwd_fp32_dense(T):
+    inp = synth.prefill_inputs("tiny", seq_len=T, heads=2, batch=2, init_std=0.02)
+    d_out, d_fin = loss_grads(inp, 10 + T)
+    say("bwd fp32 d=64", T)
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label=f"bwd fp32 T={T}")
+
+
+def test_bwd_fp32_d128():
+    inp = synth.prefill_inputs("tiny", seq_len=100, heads=2, head_dim=128, init_std=0.02)
+    d_out, d_fin = loss_grads(inp, 3)
+    say("bwd fp32 d=128")
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label="bwd fp32 d=128")
+
+
+@pytest.mark.parametrize("T", [15, 17, 333])
+@pytest.mark.parametrize("dim", [64, 128])
+def test_bwd_bf16_dense(T, dim):
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=T, heads=3, head_dim=dim, batch=2,
+                               seed=40 + T)
+    d_out, d_fin = loss_grads(inp, 20 + T)
+    say("bwd bf16", T, dim)
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label=f"bwd bf16 T={T} d={dim}")
+
+
+def test_bwd_packed_ragged():
+    lens = [0, 1, 16, 17, 50, 0, 200]
+    w = synth.WORKLOADS["varlen_16"]
+    parts = [synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=3, seed=600 + i)
+             for i, n in enumerate(lens)]
+    cat = lambda key: torch.cat([p[key] for p in parts], dim=1)
+    inp = {key: cat(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+    inp["initial_state"] = torch.cat([p["initial_state"] for p in parts])
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    d_out, d_fin = loss_grads(inp, 7)
+    say("bwd packed", lens)
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label="bwd packed")
+    # an empty sequence passes d_final_state straight through
+    assert torch.equal(g["d_initial_state"][0].cpu(), d_fin[0])
+    assert torch.equal(g["d_initial_state"][5].cpu(), d_fin[5])
+
+
+def test_bwd_without_states():
+    """No initial state, no final-state gradient, no initial-state gradient."""
+    inp = synth.prefill_inputs("prefill_4k", seq_len=300, heads=2)
+    assert inp["initial_state"] is None
+    d_out, _ = loss_grads(inp, 8)
+    say("bwd no states")
+    g = run_gpu(inp, d_out, None, output_initial_state_grad=False)
+    assert g["d_initial_state"] is None
+    compare(inp, g, oracle_grads(inp, d_out, None), label="bwd no states")
+
+
+def test_bwd_deterministic():
+    inp = synth.prefill_inputs("k3_prefill_32k", seq_len=500, heads=4, seed=9)
+    d_out, d_fin = loss_grads(inp, 9)
+    say("bwd determinism")
+    g1 = run_gpu(inp, d_out, d_fin)
+    g2 = run_gpu(inp, d_out, d_fin)
+    for name in GRADS + ("d_initial_state",):
+        assert torch.equal(g1[name], g2[name]), name
+
+
+def test_bwd_prefill_4k_sampled_heads():
+    """The 4,096-token x 32-head layer: the full launch, three heads against
+    the oracle."""
+    inp = synth.prefill_inputs("prefill_4k")
+    d_out, d_fin = loss_grads(inp, 11)
+    say("bwd prefill_4k")
+    g = run_gpu(inp, d_out, d_fin)
+    heads = [0, 15, 31]
+    compare(inp, g, oracle_grads(inp, d_out, d_fin, heads), heads=heads, label="bwd prefill_4k")
+
+
+def test_bwd_k3_prefill_32k_sampled_heads():
+    """The 32,768-token x 96-head K3 shape: the full launch, two heads over
+    all tokens against the oracle."""
+    inp = synth.prefill_inputs("k3_prefill_32k")
+    d_out, d_fin = loss_grads(inp, 12)
+    say("bwd k3 32k")
+    g = run_gpu(inp, d_out, d_fin)
+    heads = [0, 95]
+    compare(inp, g, oracle_grads(inp, d_out, d_fin, heads, threads=2), heads=heads,
+            label="bwd k3 32k")
