@@ -24,6 +24,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
        [--skip-decode]        (decode workload shrunk to one session-head; for
                                counter passes on kda_chunk_fwd only)
+       [--backward [--bwd-workload k3_prefill_32k|prefill_4k]]
+                              (instead: kda_chunk_bwd, the gradients of the
+                               prefill, on its own JSON line)
        [--segments G [--seg-workload long_1m|prefill_4k]]
                               (instead: kda_chunk_fwd_segmented with G requested
                                segments on one long sequence, kda_chunk_fwd
@@ -43,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 # d=128, chunk 32: 6 d^2 for [K+; Q+] S and Kend^T Delta, plus 24,576 for the
 # lower-triangular intra-chunk products (A, Mqk, Delta, Mqk Delta)
 PREFILL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
@@ -160,6 +164,85 @@ def attainable_peaks(torch):
             "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
 
 
+def bwd_bytes(T_tokens, H, d, n_seqs, esz=2):
+    """Algorithmic HBM bytes of one kda_chunk_bwd: read q, k, v, d_out (esz),
+    log_alpha (fp32), beta, the initial state and the final-state gradient;
+    write dq, dk, dv (esz), dlog_alpha (fp32), dbeta and the initial-state
+    gradient.  The workspace of chunk states it writes and reads back is
+    traffic the method adds, not algorithmic bytes."""
+    per_token_head = (4 * d * esz + 4 * d + 4) + (3 * d * esz + 4 * d + 4)
+    return T_tokens * H * per_token_head + 3 * n_seqs * H * d * d * 4
+
+
+def bench_backward(torch, args):
+    """kda_chunk_bwd on a prefill workload (inputs and the loss gradients
+    seeded, resident in HBM), timed alone with HIP events."""
+    import synth
+    import gated_delta_rule_81_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.bwd_workload]
+    log("generating", w.notes)
+    inp = synth.prefill_inputs(w)
+    P = {key: inp[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
+    s0 = inp["initial_state"]
+    s0 = None if s0 is None else s0.to(dev)
+    gen = torch.Generator().manual_seed(w.seed + 100)
+    T, H, D = w.seq_len * w.batch, w.heads, w.head_dim
+    d_out = torch.randn(w.batch, w.seq_len, H, D, generator=gen).to(P["q"].dtype).to(dev)
+    d_fin = (torch.randn(w.batch, H, D, D, generator=gen) * 0.1).to(dev)
+    ws = torch.empty(kda.bwd_workspace_size(T, w.batch, H, D), dtype=torch.uint8, device=dev)
+    grads = kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0,
+                      workspace=ws, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    log(f"timing {K} x kda_chunk_bwd")
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(K):
+        step()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
+    avg = sum(ms) / K
+    log(f"kda_chunk_bwd: avg {avg:.3f} ms (min {min(ms):.3f})")
+    nbytes = bwd_bytes(T, H, D, w.batch)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    # per token-head, in multiply-adds: the forward recompute (K+ S0 and
+    # Ke^T Delta: 2 d^2) and the gradient pass (K+ S0, Ke dS, dO S0^T,
+    # dX S0^T, Delta dS^T and the state gradient's two products: 7 d^2), plus
+    # the 16 x 16 x d products of the 16-token chunks (224 d); flop = 2 x that
+    flop = T * H * (18 * D * D + 448 * D)
+    tfl = flop / (avg * 1e-3) / 1e12
+    return {
+        "metric": f"KDA chunked backward tokens/s ({w.notes})",
+        "value": T / (avg * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"kda_chunk_bwd {w.name}: {w.notes}; fp32 arithmetic, "
+                               "16-token chunks", "tokens": T, "heads": H, "head_dim": D},
+        "roofline": {"bound": "mfma", "achieved": tfl, "peak": FP32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tfl / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "hbm_gbs_algorithmic": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
+        "kernel_ms_avg": avg, "kernel_ms_min": min(ms), "algorithmic_bytes": nbytes,
+        "flop_per_launch": flop,
+        "cpu_baseline": None,
+    }
+
+
 def bench_segmented(torch, args):
     """kda_chunk_fwd_segmented on one long sequence (B=1), inputs drawn on the
     device, with kda_chunk_fwd on the same input timed beside it."""
@@ -255,6 +338,11 @@ def main():
                          "on one long sequence instead (kda_chunk_fwd timed beside it)")
     ap.add_argument("--seg-workload", default="long_1m", choices=["long_1m", "prefill_4k"],
                     help="the sequence --segments runs on")
+    ap.add_argument("--backward", action="store_true",
+                    help="time kda_chunk_bwd (the prefill's gradients) instead")
+    ap.add_argument("--bwd-workload", default="k3_prefill_32k",
+                    choices=["k3_prefill_32k", "prefill_4k"],
+                    help="the prefill workload --backward runs on")
     args = ap.parse_args()
     if args.scalar_gate and args.snapshot_every:
         ap.error("--scalar-gate and --snapshot-every time different entry points; pick one")
@@ -270,6 +358,9 @@ def main():
         return
     if args.segments > 0:
         print(json.dumps(bench_segmented(torch, args)), flush=True)
+        return
+    if args.backward:
+        print(json.dumps(bench_backward(torch, args)), flush=True)
         return
 
     import synth

@@ -142,6 +142,16 @@ __device__ __forceinline__ f32x4 mm_ldst_tile(f32x4 acc, const float *At, int ld
     return acc;
 }
 
+// Four consecutive elements as fp32 (p 8-byte aligned for bf16, 16 for fp32).
+__device__ __forceinline__ f32x4 load4(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+__device__ __forceinline__ f32x4 load4(const bf16 *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                 static_cast<float>(x[3])};
+}
+
 // Keeps the scheduler from hoisting the LDS reads of later products above
 // this point (which would hold their operands in registers early).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -196,17 +206,23 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     auto prep = [&](int c, bool with_grad) -> int {
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
-        for (int idx = tid; idx < kBC * D; idx += G::THREADS) {
-            const int tok = idx / D, ch = idx % D;
+        {  // thread tid: four consecutive channels of one row (16 x D = 4 x THREADS)
+            const int tok = tid / (D / 4), ch = 4 * (tid % (D / 4));
             const bool ok = tok < nval;
             const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
-            sQp[tok * LD + ch] = ok ? to_f32(q[gi]) : 0.f;
-            sKp[tok * LD + ch] = ok ? to_f32(k[gi]) : 0.f;
-            sV[tok * LD + ch] = ok ? to_f32(v[gi]) : 0.f;
-            sG[tok * LD + ch] = ok ? log_alpha[gi] : 0.f;
-            if (with_grad) sDO[tok * LD + ch] = ok ? to_f32(d_out[gi]) : 0.f;
+            const f32x4 z = zero4();
+            const f32x4 rq = ok ? load4(q + gi) : z, rk = ok ? load4(k + gi) : z;
+            const f32x4 rv = ok ? load4(v + gi) : z;
+            const f32x4 rg = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + gi) : z;
+            const f32x4 ro = with_grad && ok ? load4(d_out + gi) : z;
+            const float rb = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
+            *reinterpret_cast<f32x4 *>(sQp + tok * LD + ch) = rq;
+            *reinterpret_cast<f32x4 *>(sKp + tok * LD + ch) = rk;
+            *reinterpret_cast<f32x4 *>(sV + tok * LD + ch) = rv;
+            *reinterpret_cast<f32x4 *>(sG + tok * LD + ch) = rg;
+            if (with_grad) *reinterpret_cast<f32x4 *>(sDO + tok * LD + ch) = ro;
+            if (tid < kBC) sBeta[tid] = rb;
         }
-        if (tid < kBC) sBeta[tid] = tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
         __syncthreads();
         if (tid < D) {
             const int ch = tid;
@@ -309,12 +325,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             dMm[t][e] = d_final ? d_final[sbase + (int64_t)(16 * t + 4 * g4 + e) * D + kcol] : 0.f;
     }
     for (int c = nch - 1; c >= 0; --c) {
+        // the chunk's entering state in both orientations, loaded before the
+        // staging so that the two sets of loads are in flight together
+        const float *S0 = ck + c * ck_stride;
+        f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            Ss[t] = *reinterpret_cast<const f32x4 *>(S0 + (int64_t)vcol * D + 16 * t + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sm[t][e] = S0[(int64_t)(16 * t + 4 * g4 + e) * D + kcol];
+        }
         const int nval = prep(c, true);
         const int64_t t0 = tbeg + (int64_t)c * kBC;
-        const float *S0 = ck + c * ck_stride;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            Ss[t] = *reinterpret_cast<const f32x4 *>(S0 + (int64_t)vcol * D + 16 * t + 4 * g4);
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
         const f32x4 pk = mm_lds_reg(zero4(), sKp, LD, Ss, lane);
         f32x4 x, xb;
@@ -368,11 +390,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             dbeta[(t0 + tid) * H + h] = s;
         }
         // key-column products (this wave's 16 key columns), with S0 in M orientation
-        f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Sm[t][e] = S0[(int64_t)(16 * t + 4 * g4 + e) * D + kcol];
         const f32x4 dqp = mm_lds_lds(mm_lds_reg(zero4(), sDO, LD, Sm, lane), sDM, LS, sKm + 16 * w,
                                      LD, lane);
         sched_fence();
