@@ -224,25 +224,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             if (tid < kBC) sBeta[tid] = rb;
         }
         __syncthreads();
-        if (tid < D) {
+        if (tid < D) {  // per channel prefix over the 16 rows
             const int ch = tid;
+            float gv[kBC];
+#pragma unroll
+            for (int tok = 0; tok < kBC; ++tok) gv[tok] = sG[tok * LD + ch];
             float acc = 0.f;
 #pragma unroll
             for (int tok = 0; tok < kBC; ++tok) {
-                acc += sG[tok * LD + ch];
+                acc += gv[tok];
                 sG[tok * LD + ch] = acc;
             }
-            const float gl = acc;
-            sGam[ch] = __expf(gl);
+            sGam[ch] = __expf(acc);
+        }
+        __syncthreads();
 #pragma unroll
-            for (int tok = 0; tok < kBC; ++tok) {
-                const float gm = sG[tok * LD + ch], eg = __expf(gm);
-                const float kr = sKp[tok * LD + ch];
-                sKp[tok * LD + ch] = kr * eg;
-                sKm[tok * LD + ch] = kr / eg;
-                sKe[tok * LD + ch] = kr * __expf(gl - gm);
-                sQp[tok * LD + ch] *= eg;
-            }
+        for (int it = 0; it < kBC * D / G::THREADS; ++it) {  // the scaled rows, all threads
+            const int idx = tid + it * G::THREADS;
+            const int tok = idx / D, ch = idx % D;
+            const float gm = sG[tok * LD + ch], eg = __expf(gm);
+            const float gl = sG[(kBC - 1) * LD + ch];
+            const float kr = sKp[tok * LD + ch];
+            sKp[tok * LD + ch] = kr * eg;
+            sKm[tok * LD + ch] = kr / eg;
+            sKe[tok * LD + ch] = kr * __expf(gl - gm);
+            sQp[tok * LD + ch] *= eg;
         }
         __syncthreads();
         if (w == 0) {
@@ -263,13 +269,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         }
         __syncthreads();
         if (w == 0 && lane < kBC) {  // column j = lane of T by forward substitution
-            const int j = lane;
+            // j through an opaque move, so the identity's per-lane constants
+            // are formed here and not kept live across the kernel
+            int j;
+            asm volatile("v_mov_b32 %0, %1" : "=v"(j) : "v"(lane));
             float col[kBC];
+            f32x4 nxt[4];  // row i + 1 of A, read while row i is solved
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = zero4();
 #pragma unroll
             for (int i = 0; i < kBC; ++i) {
+                f32x4 cur[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+                if (i + 1 < kBC) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        nxt[q4] = *reinterpret_cast<const f32x4 *>(sA + (i + 1) * LS + 4 * q4);
+                }
                 float s = i == j ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) s -= sA[i * LS + m] * col[m];
+                for (int m = 0; m < i; ++m) s -= cur[m / 4][m % 4] * col[m];
                 col[i] = s;
                 sT[i * LS + j] = s;
                 sTt[j * LS + i] = s;
