@@ -58,10 +58,15 @@ struct BwdCfg {
     static constexpr int oQp = 0, oKp = ROW, oKm = 2 * ROW, oKe = 3 * ROW, oG = 4 * ROW,
                          oV = 5 * ROW, oDO = 6 * ROW, oDl = 7 * ROW, oLm = 8 * ROW,
                          oDX = 9 * ROW;
+    // P shares A's space (A is dead once T is formed) and dM shares M's (M is
+    // last read before the barrier that precedes dM)
     static constexpr int oBr = 10 * ROW, oA = oBr + SQ, oM = oA + SQ, oT = oM + SQ,
-                         oTt = oT + SQ, oP = oTt + SQ, oDM = oP + SQ;
-    static constexpr int oGam = oDM + SQ, oBeta = oGam + D, oDB = oBeta + kBC;
-    static constexpr int FLOATS = oDB + (W + 1) * kBC;
+                         oTt = oT + SQ, oP = oA, oDM = oM;
+    static constexpr int oGam = oTt + SQ, oBeta = oGam + D, oDB = oBeta + kBC;
+    // dL/dS at the chunk end, stored [v][k] (the M orientation), for the
+    // products that contract over d_v
+    static constexpr int LDSD = D + 4, oSD = oDB + (W + 1) * kBC;
+    static constexpr int FLOATS = oSD + D * LDSD;
 };
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
@@ -180,6 +185,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *sLm = sm + G::oLm, *sDX = sm + G::oDX, *sBr = sm + G::oBr, *sA = sm + G::oA;
     float *sM = sm + G::oM, *sT = sm + G::oT, *sTt = sm + G::oTt, *sP = sm + G::oP;
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
+    float *sSD = sm + G::oSD;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
     const int n = blockIdx.x / H, h = blockIdx.x % H;
@@ -334,17 +340,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
 
     // ------------------------------------------------------------ pass 2
     f32x4 dSs[NT];  // dL/dS at the chunk end, S orientation (value column vcol)
-    f32x4 dMm[NT];  // the same in M orientation: [v = 16j + 4g + e][k = kcol]
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < NT; ++t)
         dSs[t] = d_final ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vcol * D +
                                                             16 * t + 4 * g4)
                          : zero4();
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dMm[t][e] = d_final ? d_final[sbase + (int64_t)(16 * t + 4 * g4 + e) * D + kcol] : 0.f;
-    }
     for (int c = nch - 1; c >= 0; --c) {
+        // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
+        // barriers separate these writes from those reads; the previous
+        // chunk's reads ended at its last barrier)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            *reinterpret_cast<f32x4 *>(sSD + vcol * G::LDSD + 16 * t + 4 * g4) = dSs[t];
         // the chunk's entering state in both orientations, loaded before the
         // staging so that the two sets of loads are in flight together
         const float *S0 = ck + c * ck_stride;
@@ -416,15 +423,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         const f32x4 xs = mm_lds_reg(zero4(), sDX, LD, Sm, lane);
         sched_fence();
         float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s1 += Sm[t][e] * dMm[t][e];
         const f32x4 pkm = mm_lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
         const f32x4 dkm = mm_ldst_lds(mm_ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
                                       LS, sKp + 16 * w, LD, lane);
         sched_fence();
-        const f32x4 dke = mm_lds_reg(zero4(), sDl, LD, dMm, lane);
+        // dKe = Delta dS_C^T and rowsum(S0 * dS_C), from dS_C[k = kcol][v] = sSD[v][kcol]
+        f32x4 dke = zero4();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(sDl + r * LD + 16 * t + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float b = sSD[(16 * t + 4 * g4 + e) * G::LDSD + kcol];
+                dke = mf(a[e], b, dke);
+                s1 += Sm[t][e] * b;
+            }
+        }
         sched_fence();
 #pragma unroll
         for (int e = 0; e < 4; ++e) s2 += dke[e] * sKe[(4 * g4 + e) * LD + kcol];
@@ -467,7 +481,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             if (tok < nval)
                 dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] = dgm[e] + above;
         }
-        // state gradient before the chunk, both orientations
+        // state gradient before the chunk
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const f32x4 u = mm_ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
@@ -475,10 +489,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
-            const f32x4 um = mm_ldst_lds(zero4(), sDO + 16 * t, LD, sQp + 16 * w, LD, lane);
-            const f32x4 ym = mm_ldst_lds(zero4(), sDX + 16 * t, LD, sKp + 16 * w, LD, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dMm[t][e] = gamk * dMm[t][e] + um[e] - ym[e];
             sched_fence();
         }
         __syncthreads();
