@@ -217,12 +217,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             const bool ok = tok < nval;
             const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
             const f32x4 z = zero4();
-            const f32x4 rq = ok ? load4(q + gi) : z, rk = ok ? load4(k + gi) : z;
+            // the forward pass (with_grad false) needs neither q nor d_out
+            const f32x4 rq = with_grad && ok ? load4(q + gi) : z, rk = ok ? load4(k + gi) : z;
             const f32x4 rv = ok ? load4(v + gi) : z;
             const f32x4 rg = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + gi) : z;
             const f32x4 ro = with_grad && ok ? load4(d_out + gi) : z;
             const float rb = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
-            *reinterpret_cast<f32x4 *>(sQp + tok * LD + ch) = rq;
+            if (with_grad) *reinterpret_cast<f32x4 *>(sQp + tok * LD + ch) = rq;
             *reinterpret_cast<f32x4 *>(sKp + tok * LD + ch) = rk;
             *reinterpret_cast<f32x4 *>(sV + tok * LD + ch) = rv;
             *reinterpret_cast<f32x4 *>(sG + tok * LD + ch) = rg;
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             sKp[tok * LD + ch] = kr * eg;
             sKm[tok * LD + ch] = kr / eg;
             sKe[tok * LD + ch] = kr * __expf(gl - gm);
-            sQp[tok * LD + ch] *= eg;
+            if (with_grad) sQp[tok * LD + ch] *= eg;
         }
         __syncthreads();
         if (w == 0) {
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 sBr[i * LS + r] = b[e];
                 sA[i * LS + r] = r < i ? sBeta[i] * b[e] : 0.f;
             }
-        } else if (w == 1) {
+        } else if (w == 1 && with_grad) {
             const f32x4 m = mm_lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
