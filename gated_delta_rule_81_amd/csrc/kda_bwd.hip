@@ -147,6 +147,169 @@ __device__ __forceinline__ f32x4 mm_ldst_tile(f32x4 acc, const float *At, int ld
     return acc;
 }
 
+// The same products with bf16 operands (fp32 accumulation) for bf16 inputs:
+// v_mfma_f32_16x16x32_bf16 for the d-long contractions (lane group g takes
+// k = 32b + 4g + e and 32b + 16 + 4g + e, e = 0..3, on both operands, so two
+// 16-row register tiles form one B fragment) and v_mfma_f32_16x16x16_bf16 for
+// the 16-long ones (lane group g takes k = 4g + e, the f32 path's order).
+__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = static_cast<bf16>(a[e]);
+        r[4 + e] = static_cast<bf16>(b[e]);
+    }
+    return r;
+}
+__device__ __forceinline__ i16x4 pack4(float a, float b, float c, float d) {
+    bf16x4 r;
+    r[0] = static_cast<bf16>(a);
+    r[1] = static_cast<bf16>(b);
+    r[2] = static_cast<bf16>(c);
+    r[3] = static_cast<bf16>(d);
+    return __builtin_bit_cast(i16x4, r);
+}
+__device__ __forceinline__ f32x4 mf32(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mf16(const i16x4 &a, const i16x4 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <bool BF>
+struct Prod;
+
+template <>
+struct Prod<false> {
+    template <int NT>
+    __device__ static f32x4 lds_reg(f32x4 acc, const float *A, int lda, const f32x4 (&B)[NT],
+                                    int lane) {
+        return mm_lds_reg(acc, A, lda, B, lane);
+    }
+    __device__ static f32x4 lds_tile(f32x4 acc, const float *A, int lda, const f32x4 &B,
+                                     int lane) {
+        return mm_lds_tile(acc, A, lda, B, lane);
+    }
+    template <int K>
+    __device__ static f32x4 lds_ldst(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
+                                     int lane) {
+        return mm_lds_ldst<K>(acc, A, lda, Bt, ldb, lane);
+    }
+    __device__ static f32x4 ldst_lds(f32x4 acc, const float *At, int lda, const float *Bm, int ldb,
+                                     int lane) {
+        return mm_ldst_lds(acc, At, lda, Bm, ldb, lane);
+    }
+    __device__ static f32x4 lds_lds(f32x4 acc, const float *A, int lda, const float *Bm, int ldb,
+                                    int lane) {
+        return mm_lds_lds(acc, A, lda, Bm, ldb, lane);
+    }
+    __device__ static f32x4 ldst_tile(f32x4 acc, const float *At, int lda, const f32x4 &B,
+                                      int lane) {
+        return mm_ldst_tile(acc, At, lda, B, lane);
+    }
+    // acc += A (16 x 16NT, row-major) x Bc, where Bc[k][j] = Bs[k * ldb] (a column of a
+    // [k][..] array at this lane's j), and s += sum_k W[k / 16][k % 16 - ...] * Bc[k][j]
+    // with W in register-tile order (row k = 16t + 4g + e); the d_v contraction of
+    // Delta dS^T together with rowsum(S0 * dS).
+    template <int NT>
+    __device__ static f32x4 lds_col(f32x4 acc, float &s, const float *A, int lda, const float *Bs,
+                                    int ldb, const f32x4 (&W)[NT], int lane) {
+        const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float b = Bs[(16 * t + 4 * g + e) * ldb];
+                acc = mf(a[e], b, acc);
+                s += W[t][e] * b;
+            }
+        }
+        return acc;
+    }
+};
+
+template <>
+struct Prod<true> {
+    template <int NT>
+    __device__ static f32x4 lds_reg(f32x4 acc, const float *A, int lda, const f32x4 (&B)[NT],
+                                    int lane) {
+        const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < NT / 2; ++b) {
+            const float *a0 = A + r * lda + 32 * b + 4 * g;
+            acc = mf32(pack8(*reinterpret_cast<const f32x4 *>(a0),
+                             *reinterpret_cast<const f32x4 *>(a0 + 16)),
+                       pack8(B[2 * b], B[2 * b + 1]), acc);
+        }
+        return acc;
+    }
+    __device__ static f32x4 lds_tile(f32x4 acc, const float *A, int lda, const f32x4 &B,
+                                     int lane) {
+        const int r = lane & 15, g = lane >> 4;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 4 * g);
+        return mf16(pack4(a[0], a[1], a[2], a[3]), pack4(B[0], B[1], B[2], B[3]), acc);
+    }
+    template <int K>
+    __device__ static f32x4 lds_ldst(f32x4 acc, const float *A, int lda, const float *Bt, int ldb,
+                                     int lane) {
+        const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < K / 32; ++b) {
+            const float *a0 = A + r * lda + 32 * b + 4 * g;
+            const float *b0 = Bt + r * ldb + 32 * b + 4 * g;
+            acc = mf32(pack8(*reinterpret_cast<const f32x4 *>(a0),
+                             *reinterpret_cast<const f32x4 *>(a0 + 16)),
+                       pack8(*reinterpret_cast<const f32x4 *>(b0),
+                             *reinterpret_cast<const f32x4 *>(b0 + 16)),
+                       acc);
+        }
+        return acc;
+    }
+    __device__ static f32x4 ldst_lds(f32x4 acc, const float *At, int lda, const float *Bm, int ldb,
+                                     int lane) {
+        const int r = lane & 15, g = lane >> 4;
+        const float *a0 = At + 4 * g * lda + r, *b0 = Bm + 4 * g * ldb + r;
+        return mf16(pack4(a0[0], a0[lda], a0[2 * lda], a0[3 * lda]),
+                    pack4(b0[0], b0[ldb], b0[2 * ldb], b0[3 * ldb]), acc);
+    }
+    __device__ static f32x4 lds_lds(f32x4 acc, const float *A, int lda, const float *Bm, int ldb,
+                                    int lane) {
+        const int r = lane & 15, g = lane >> 4;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 4 * g);
+        const float *b0 = Bm + 4 * g * ldb + r;
+        return mf16(pack4(a[0], a[1], a[2], a[3]),
+                    pack4(b0[0], b0[ldb], b0[2 * ldb], b0[3 * ldb]), acc);
+    }
+    __device__ static f32x4 ldst_tile(f32x4 acc, const float *At, int lda, const f32x4 &B,
+                                      int lane) {
+        const int r = lane & 15, g = lane >> 4;
+        const float *a0 = At + 4 * g * lda + r;
+        return mf16(pack4(a0[0], a0[lda], a0[2 * lda], a0[3 * lda]),
+                    pack4(B[0], B[1], B[2], B[3]), acc);
+    }
+    template <int NT>
+    __device__ static f32x4 lds_col(f32x4 acc, float &s, const float *A, int lda, const float *Bs,
+                                    int ldb, const f32x4 (&W)[NT], int lane) {
+        const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int b = 0; b < NT / 2; ++b) {
+            const float *a0 = A + r * lda + 32 * b + 4 * g;
+            f32x4 c0, c1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c0[e] = Bs[(32 * b + 4 * g + e) * ldb];
+                c1[e] = Bs[(32 * b + 16 + 4 * g + e) * ldb];
+                s += W[2 * b][e] * c0[e] + W[2 * b + 1][e] * c1[e];
+            }
+            acc = mf32(pack8(*reinterpret_cast<const f32x4 *>(a0),
+                             *reinterpret_cast<const f32x4 *>(a0 + 16)),
+                       pack8(c0, c1), acc);
+        }
+        return acc;
+    }
+};
+
 // Four consecutive elements as fp32 (p 8-byte aligned for bf16, 16 for fp32).
 __device__ __forceinline__ f32x4 load4(const float *p) {
     return *reinterpret_cast<const f32x4 *>(p);
@@ -178,6 +341,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *__restrict__ dbeta, float *__restrict__ d_initial, float *__restrict__ ckpt,
     int seq_len, int total_tokens, int H) {
     typedef BwdCfg<D> G;
+    typedef Prod<sizeof(T) == 2> PR;  // bf16 inputs: bf16 products, fp32 accumulation
     constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
     __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
     float *sQp = sm + G::oQp, *sKp = sm + G::oKp, *sKm = sm + G::oKm, *sKe = sm + G::oKe;
@@ -259,7 +423,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         }
         __syncthreads();
         if (w == 0) {
-            const f32x4 b = mm_lds_ldst<D>(zero4(), sKp, LD, sKm, LD, lane);
+            const f32x4 b = PR::template lds_ldst<D>(zero4(), sKp, LD, sKm, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
@@ -267,7 +431,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 sA[i * LS + r] = r < i ? sBeta[i] * b[e] : 0.f;
             }
         } else if (w == 1 && with_grad) {
-            const f32x4 m = mm_lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
+            const f32x4 m = PR::template lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
@@ -320,17 +484,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4 *>(ck + c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4) =
                 Ss[t];
-        const f32x4 pk = mm_lds_reg(zero4(), sKp, LD, Ss, lane);
+        const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
         f32x4 xb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             xb[e] = sBeta[tok] * (sV[tok * LD + vcol] - pk[e]);
         }
-        const f32x4 dl = mm_lds_tile(zero4(), sT, LS, xb, lane);
+        const f32x4 dl = PR::lds_tile(zero4(), sT, LS, xb, lane);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const f32x4 u = mm_ldst_tile(zero4(), sKe + 16 * t, LD, dl, lane);
+            const f32x4 u = PR::ldst_tile(zero4(), sKe + 16 * t, LD, dl, lane);
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ss[t][e] = gm[e] * Ss[t][e] + u[e];
@@ -366,7 +530,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         const int nval = prep(c, true);
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
-        const f32x4 pk = mm_lds_reg(zero4(), sKp, LD, Ss, lane);
+        const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
         f32x4 x, xb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -374,12 +538,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             x[e] = sV[tok * LD + vcol] - pk[e];
             xb[e] = sBeta[tok] * x[e];
         }
-        const f32x4 dl = mm_lds_tile(zero4(), sT, LS, xb, lane);
+        const f32x4 dl = PR::lds_tile(zero4(), sT, LS, xb, lane);
         sched_fence();
-        f32x4 ddl = mm_ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
-        ddl = mm_lds_reg(ddl, sKe, LD, dSs, lane);
+        f32x4 ddl = PR::ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
+        ddl = PR::lds_reg(ddl, sKe, LD, dSs, lane);
         sched_fence();
-        const f32x4 lam = mm_lds_tile(zero4(), sTt, LS, ddl, lane);
+        const f32x4 lam = PR::lds_tile(zero4(), sTt, LS, ddl, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
@@ -393,7 +557,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         }
         __syncthreads();
         if (w == 0) {  // dA, P = diag(b) dA and the K+K-^T part of db
-            const f32x4 ld = mm_lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
+            const f32x4 ld = PR::template lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
@@ -403,7 +567,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 if (r == 0) sDB[G::W * kBC + i] = pb;
             }
         } else if (w == 1) {  // dM = Tril(dO Delta^T)
-            const f32x4 od = mm_lds_ldst<D>(zero4(), sDO, LD, sDl, LD, lane);
+            const f32x4 od = PR::template lds_ldst<D>(zero4(), sDO, LD, sDl, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
@@ -418,28 +582,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             dbeta[(t0 + tid) * H + h] = s;
         }
         // key-column products (this wave's 16 key columns), with S0 in M orientation
-        const f32x4 dqp = mm_lds_lds(mm_lds_reg(zero4(), sDO, LD, Sm, lane), sDM, LS, sKm + 16 * w,
+        const f32x4 dqp = PR::lds_lds(PR::lds_reg(zero4(), sDO, LD, Sm, lane), sDM, LS, sKm + 16 * w,
                                      LD, lane);
         sched_fence();
-        const f32x4 xs = mm_lds_reg(zero4(), sDX, LD, Sm, lane);
+        const f32x4 xs = PR::lds_reg(zero4(), sDX, LD, Sm, lane);
         sched_fence();
         float s1 = 0.f, s2 = 0.f;
-        const f32x4 pkm = mm_lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
-        const f32x4 dkm = mm_ldst_lds(mm_ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
+        const f32x4 pkm = PR::lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
+        const f32x4 dkm = PR::ldst_lds(PR::ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
                                       LS, sKp + 16 * w, LD, lane);
         sched_fence();
         // dKe = Delta dS_C^T and rowsum(S0 * dS_C), from dS_C[k = kcol][v] = sSD[v][kcol]
-        f32x4 dke = zero4();
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(sDl + r * LD + 16 * t + 4 * g4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float b = sSD[(16 * t + 4 * g4 + e) * G::LDSD + kcol];
-                dke = mf(a[e], b, dke);
-                s1 += Sm[t][e] * b;
-            }
-        }
+        const f32x4 dke = PR::lds_col(zero4(), s1, sDl, LD, sSD + kcol, G::LDSD, Sm, lane);
         sched_fence();
 #pragma unroll
         for (int e = 0; e < 4; ++e) s2 += dke[e] * sKe[(4 * g4 + e) * LD + kcol];
@@ -485,8 +639,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // state gradient before the chunk
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const f32x4 u = mm_ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
-            const f32x4 y = mm_ldst_lds(zero4(), sKp + 16 * t, LD, sDX + 16 * w, LD, lane);
+            const f32x4 u = PR::ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
+            const f32x4 y = PR::ldst_lds(zero4(), sKp + 16 * t, LD, sDX + 16 * w, LD, lane);
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
