@@ -226,17 +226,29 @@ def bench_backward(torch, args):
     # the 16 x 16 x d products of the 16-token chunks (224 d); flop = 2 x that
     flop = T * H * (18 * D * D + 448 * D)
     tfl = flop / (avg * 1e-3) / 1e12
+    # bf16 inputs: bf16 products with fp32 accumulation, so the roofline is the
+    # bf16 one, whose ridge (~315 flop/B) lies above this kernel's 125 flop/B
+    # of algorithmic intensity: HBM-bound in principle
+    bf = P["q"].dtype == torch.bfloat16
+    mpeak = BF16_DENSE_PEAK_TFLOPS if bf else FP32_MFMA_PEAK_TFLOPS
+    if bf:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                "mfma_tflops_algorithmic": tfl, "mfma_frac": tfl / mpeak}
+    else:
+        roof = {"bound": "mfma", "achieved": tfl, "peak": mpeak, "unit": "TFLOP/s",
+                "frac": tfl / mpeak, "traffic": None, "hbm_gbs_algorithmic": gbs,
+                "hbm_frac": gbs / HBM_PEAK_GBS}
     return {
         "metric": f"KDA chunked backward tokens/s ({w.notes})",
         "value": T / (avg * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf else "f32",
         "data": "synthetic",
-        "config": {"workload": f"kda_chunk_bwd {w.name}: {w.notes}; fp32 arithmetic, "
-                               "16-token chunks", "tokens": T, "heads": H, "head_dim": D},
-        "roofline": {"bound": "mfma", "achieved": tfl, "peak": FP32_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tfl / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
-                     "hbm_gbs_algorithmic": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
+        "config": {"workload": f"kda_chunk_bwd {w.name}: {w.notes}; "
+                               + ("bf16 products, fp32 accumulation" if bf else "fp32 products")
+                               + ", 16-token chunks", "tokens": T, "heads": H, "head_dim": D},
+        "roofline": roof,
         "kernel_ms_avg": avg, "kernel_ms_min": min(ms), "algorithmic_bytes": nbytes,
         "flop_per_launch": flop,
         "cpu_baseline": None,
