@@ -51,6 +51,8 @@ FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
 # lower-triangular intra-chunk products (A, Mqk, Delta, Mqk Delta)
 PREFILL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_b256.traffic.json")
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
 
 
 def log(*a):
@@ -73,12 +75,12 @@ def decode_bytes(B, H, d, esz=2, gate_width=None):
     return B * H * (2 * d * d * 4 + 3 * d * esz + 4 * gw + 4 + d * esz)
 
 
-def source_digest():
-    """sha256 of the prefill kernel's source with comments and blank lines
-    removed, so that comment edits keep the counter summary valid."""
+def source_digest(names=("kda_chunk.hip", "kda_device.h")):
+    """sha256 of a kernel's sources (the prefill's by default) with comments and
+    blank lines removed, so that comment edits keep a counter summary valid."""
     import re
     h = hashlib.sha256()
-    for name in ("kda_chunk.hip", "kda_device.h"):
+    for name in names:
         with open(os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc", name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -87,15 +89,16 @@ def source_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per kda_chunk_fwd launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def measured_traffic(path=TRAFFIC_FILE, names=("kda_chunk.hip", "kda_device.h")):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (the
+    prefill's by default), if it was taken on the current kernel source; else
+    None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
-    if doc.get("kernel_source_sha256") != source_digest():
+    if doc.get("kernel_source_sha256") != source_digest(names):
         return None
     return doc.get("hbm_bytes_per_launch")
 
@@ -468,6 +471,8 @@ def main():
     dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
     pre_tflops = PREFILL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
     traffic = measured_traffic() if every == 0 and not sg else None
+    dec_traffic = (measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
+                   if not sg and not args.skip_decode else None)
 
     result = {
         "metric": "KDA chunked-fwd tokens/s (H=96,d=128,T=32K); decode state-update HBM GB/s",
@@ -505,7 +510,7 @@ def main():
                    "algorithmic_bytes": dbytes, "tokens_per_s": w_dec.batch / (dec_avg * 1e-3),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                                "traffic": None}},
+                                "traffic": dec_traffic}},
     }
     if not args.no_cpu_baseline:
         threads = len(os.sched_getaffinity(0))
