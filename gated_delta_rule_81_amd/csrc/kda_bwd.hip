@@ -430,41 +430,42 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 sBr[i * LS + r] = b[e];
                 sA[i * LS + r] = r < i ? sBeta[i] * b[e] : 0.f;
             }
+            // A is this wave's own LDS writes: a wave fence, no workgroup barrier
+            wave_lds_fence();
+            if (lane < kBC) {  // column j = lane of T by forward substitution
+                // j through an opaque move, so the identity's per-lane constants
+                // are formed here and not kept live across the kernel
+                int j;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(j) : "v"(lane));
+                float col[kBC];
+                f32x4 nxt[4];  // row i + 1 of A, read while row i is solved
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = zero4();
+#pragma unroll
+                for (int i = 0; i < kBC; ++i) {
+                    f32x4 cur[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
+                    if (i + 1 < kBC) {
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            nxt[q4] = *reinterpret_cast<const f32x4 *>(sA + (i + 1) * LS + 4 * q4);
+                    }
+                    float s = i == j ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) s -= cur[m / 4][m % 4] * col[m];
+                    col[i] = s;
+                    sT[i * LS + j] = s;
+                    sTt[j * LS + i] = s;
+                    sched_fence();
+                }
+            }
         } else if (w == 1 && with_grad) {
             const f32x4 m = PR::template lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
                 sM[i * LS + r] = r <= i ? m[e] : 0.f;
-            }
-        }
-        __syncthreads();
-        if (w == 0 && lane < kBC) {  // column j = lane of T by forward substitution
-            // j through an opaque move, so the identity's per-lane constants
-            // are formed here and not kept live across the kernel
-            int j;
-            asm volatile("v_mov_b32 %0, %1" : "=v"(j) : "v"(lane));
-            float col[kBC];
-            f32x4 nxt[4];  // row i + 1 of A, read while row i is solved
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = zero4();
-#pragma unroll
-            for (int i = 0; i < kBC; ++i) {
-                f32x4 cur[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-                if (i + 1 < kBC) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        nxt[q4] = *reinterpret_cast<const f32x4 *>(sA + (i + 1) * LS + 4 * q4);
-                }
-                float s = i == j ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) s -= cur[m / 4][m % 4] * col[m];
-                col[i] = s;
-                sT[i * LS + j] = s;
-                sTt[j * LS + i] = s;
-                sched_fence();
             }
         }
         __syncthreads();
