@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     const T *__restrict__ d_out, const float *__restrict__ d_final, T *__restrict__ dq,
     T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dlog_alpha,
     float *__restrict__ dbeta, float *__restrict__ d_initial, float *__restrict__ ckpt,
-    int seq_len, int total_tokens, int H) {
+    int seq_len, int total_tokens, int H, int states_ready) {
     typedef BwdCfg<D> G;
     typedef Prod<sizeof(T) == 2> PR;  // bf16 inputs: bf16 products, fp32 accumulation
     constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
@@ -473,13 +473,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     };
 
     // ------------------------------------------------------------ pass 1
+    // (skipped when an earlier launch on the stream, the prefill kernel's
+    // states mode, has already written every chunk's entering state)
     f32x4 Ss[NT];  // S0 of the chunk: [k = 16t + 4g + e][v = vcol]
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         Ss[t] = initial_state ? *reinterpret_cast<const f32x4 *>(
                                     initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * g4)
                               : zero4();
-    for (int c = 0; c < nch; ++c) {
+    for (int c = 0; !states_ready && c < nch; ++c) {
         prep(c, false);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -666,12 +668,23 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
     const int64_t units = (int64_t)num_seqs * H;
     if (units == 0) return 0;
     if (units > (int64_t)1 << 30) return -1;
+    // The chunk-entering states from the prefill kernel (32-token chunks, all
+    // CUs' worth of parallelism per head as in the forward) where it supports
+    // the configuration; otherwise pass 1 of this kernel recomputes them.
+    int ready = 0;
+    if ((sizeof(T) == 2 || D == 64) && (int64_t)H * D * 4 * 64 <= INT32_MAX) {
+        if (launch_chunk_states(q, k, v, log_alpha, beta, initial_state, cu_seqlens, ckpt,
+                                num_seqs, seq_len, total_tokens, H, D,
+                                sizeof(T) == 2 ? kDtypeBf16 : kDtypeF32, stream) != 0)
+            return -1;
+        ready = 1;
+    }
     hipLaunchKernelGGL((chunk_bwd_kernel<T, D>), dim3((unsigned)units),
                        dim3(BwdCfg<D>::THREADS), 0, stream, static_cast<const T *>(q),
                        static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
                        initial_state, cu_seqlens, static_cast<const T *>(d_out), d_final,
                        static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv),
-                       dlog_alpha, dbeta, d_initial, ckpt, seq_len, total_tokens, H);
+                       dlog_alpha, dbeta, d_initial, ckpt, seq_len, total_tokens, H, ready);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -402,8 +402,14 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
 //   kModeState  no outputs (out is not used): final states only;
 //   kModeMap    no outputs, zero values (v is not used) and every workgroup
 //               starting from S = I: the final state is the sequence's state
-//               transition (transposed like every state).
-constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2;
+//               transition (transposed like every state);
+//   kModeStates no outputs: the state entering every 16-token block of each
+//               sequence (the checkpoints of the chunked backward) goes to
+//               `snapshots`, slot tbeg / 16 + n + j for block j of sequence n,
+//               [slot][H][d_v][d_k].  A 32-token chunk's second block enters
+//               with e^{Gamma_15} S + (K e^{Gamma_15 - Gamma})_{0..15}^T Delta_0,
+//               the block-0 half of the chunk's own transition.
+constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
 template <typename T, int D, int DVS, bool SG, int MODE>
 __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -620,6 +626,12 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     *reinterpret_cast<f32x4 *>(pGam + c) =
                         f32x4{erho[0] * ep1[0], erho[1] * ep1[1], erho[2] * ep1[2],
                               erho[3] * ep1[3]};
+                    // e^{rho} for the mid-chunk state (states mode: the O staging
+                    // area is free, one D-float slot per buffer set)
+                    if constexpr (MODE == kModeStates)
+                        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(smem + G::oO) +
+                                                   (tick & 1) * D + c) =
+                            f32x4{erho[0], erho[1], erho[2], erho[3]};
                 }
                 // (K e^{rho - Gamma})^T, channel rows, token pairs (r, r + 1) of
                 // both blocks: the even lane stores channels c, c + 1, the odd
@@ -764,7 +776,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     // snap_base counts the snapshots of the sequences before it (their lengths
     // clamped exactly as their own workgroups clamp them).
     int snap_base = 0;
-    if (snapshots) {
+    if (MODE != kModeStates && snapshots) {
         if (cu_seqlens) {
             int cnt = 0;
             for (int m = lane; m < n; m += 64) {
@@ -887,6 +899,33 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // S <- Diag(gamma) S + Diag(f1) (K e^{rho - Gamma})^T Delta
             const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
             const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
+            if constexpr (MODE == kModeStates) {
+                // the chunk's entering state (block 2 m) and, if the sequence has
+                // a block 2 m + 1, the state after block 0:
+                // e^{rho} S + (K e^{rho - Gamma})_{block 0}^T Delta_0
+                const int m2 = 2 * (tick - 1);
+                const int nblk = (int)((tend - tbeg + kBS - 1) / kBS);
+                const bool mid = m2 + 1 < nblk;
+                const typename SM::Frag Dbm = SM::b(Dl[0], zero4());
+                const float *cRho =
+                    reinterpret_cast<const float *>(smem + G::oO) + ((tick - 1) & 1) * D;
+                float *dst = snapshots + ((tbeg / kBS + n + m2) * H + h) * (int64_t)D * D +
+                             (int64_t)vcol * D + 4 * l4;
+                const int64_t blk = (int64_t)H * D * D;
+#pragma unroll
+                for (int t = 0; t < G::NRT; ++t) {
+                    *reinterpret_cast<f32x4 *>(dst + 16 * t) = Sm[t];
+                    if (mid) {
+                        const f32x4 acc =
+                            SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Dbm);
+                        const f32x4 rh = *reinterpret_cast<const f32x4 *>(cRho + 16 * t + 4 * l4);
+                        f32x4 sm;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sm[e] = rh[e] * Sm[t][e] + acc[e];
+                        *reinterpret_cast<f32x4 *>(dst + blk + 16 * t) = sm;
+                    }
+                }
+            }
 #pragma unroll
             for (int t = 0; t < G::NRT; ++t) {
                 f32x4 acc = SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Db0);
@@ -900,7 +939,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // a snapshot after every snap_every tokens (a multiple of the chunk
             // length, so only full chunks end on one)
             const int64_t done = (int64_t)tick * kC;
-            if (snapshots && done % snap_every == 0 && done <= tend - tbeg) {
+            if (MODE != kModeStates && snapshots && done % snap_every == 0 &&
+                done <= tend - tbeg) {
                 const int64_t idx = snap_base + done / snap_every - 1;
                 if (idx < snap_cap) {
                     float *dst = snapshots + (idx * H + h) * D * D + (int64_t)vcol * D + 4 * l4;
@@ -956,6 +996,17 @@ int launch_dtype(const void *q, const void *k, const void *v, const float *log_a
 }
 
 }  // namespace
+
+int launch_chunk_states(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *initial_state,
+                        const int32_t *cu_seqlens, float *states, int32_t num_seqs,
+                        int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
+                        int dtype, hipStream_t stream) {
+    if (dtype != kDtypeBf16 && head_dim != 64) return -1;
+    return launch_dtype<false, kModeStates>(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
+                                            nullptr, nullptr, states, kC, 0, num_seqs, seq_len,
+                                            total_tokens, num_heads, head_dim, dtype, stream);
+}
 
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,
                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,

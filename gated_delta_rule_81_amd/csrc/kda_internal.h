@@ -35,6 +35,18 @@ int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *l
                      int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
                      int scalar_gate, int init_identity, hipStream_t stream);
 
+// The state entering every 16-token block of every sequence, written to
+// `states` as the chunked backward's checkpoints (slot tbeg / 16 + n + j for
+// block j of sequence n, [slot][H][d_v][d_k]; chunk_bwd_workspace_floats(...)
+// floats), computed by the prefill kernel without outputs.  Sequences as for
+// launch_chunk_fwd.  bf16 at head_dim 64 or 128, fp32 at 64.  Returns 0, or -1
+// if the launch failed or the configuration is not one of these.
+int launch_chunk_states(const void *q, const void *k, const void *v, const float *log_alpha,
+                        const float *beta, const float *initial_state,
+                        const int32_t *cu_seqlens, float *states, int32_t num_seqs,
+                        int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
+                        int dtype, hipStream_t stream);
+
 // Tokens per chunk of the prefill; snapshot intervals are multiples of it.
 constexpr int kChunkTokens = 32;
 

@@ -224,8 +224,11 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  * chunkwise form ([Kimi-Linear], the section on KDA's per-channel forgetting:
  * training runs as matrix products instead of a token-serial RNN) but state
  * no gradient; this is the exact derivative of the recurrence of kda_chunk_fwd
- * (up to rounding), computed chunk by chunk (16 tokens) in reverse with each
- * chunk's entering state recomputed by a forward pass in the same call.
+ * (up to rounding), computed chunk by chunk (16 tokens) in reverse from each
+ * chunk's entering state, which a forward pass in the same call writes to the
+ * workspace first (bf16 at d 64 or 128 and fp32 at d 64: the prefill kernel
+ * in a states-only mode, 32 tokens per step; fp32 at d 128: 16-token steps
+ * inside the backward kernel).
  *
  * Inputs: q, k, v, log_alpha, beta, initial_state, cu_seqlens, batch, seq_len,
  * num_heads, head_dim_k, head_dim_v, num_seqs and dtype exactly as given to
@@ -242,7 +245,8 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state; contents
  * on return are unspecified.  No output may overlap an input, another output or
  * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
- * bf16 (fp32 arithmetic inside for both).  Same numerics contract as
+ * bf16 (bf16 inputs: bf16 matrix products with fp32 accumulation; fp32 inputs:
+ * fp32 throughout).  Same numerics contract as
  * kda_chunk_fwd.  Returns KDA_OK or a kda_status error code.
  */
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -165,3 +165,60 @@ def test_bwd_k3_prefill_32k_sampled_heads():
     heads = [0, 95]
     compare(inp, g, oracle_grads(inp, d_out, d_fin, heads, threads=2), heads=heads,
             label="bwd k3 32k")
+
+
+def packed_parts(lens, make):
+    parts = [make(i, n) for i, n in enumerate(lens)]
+    cat = lambda key: torch.cat([p[key] for p in parts], dim=1)
+    inp = {key: cat(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+    inp["initial_state"] = torch.cat([p["initial_state"] for p in parts])
+    inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    return inp
+
+
+@pytest.mark.parametrize("case", ["bf16_d128", "bf16_d64", "fp32_d64", "fp32_d128"])
+def test_bwd_checkpoints_are_block_states(case):
+    """White-box: on return the workspace holds the state entering every
+    16-token block of every sequence (slot t0 // 16 + n + j for block j of
+    sequence n starting at token t0, [slot][H][d_v][d_k]).  For bf16 and for
+    fp32 at d = 64 the prefill kernel's states mode writes them (32-token chunks:
+    even blocks are chunk-entering states, odd blocks the state after a chunk's
+    first 16 tokens); fp32 at d = 128 recomputes them inside the backward
+    kernel.  Each is checked against the oracle's state after the first 16 j
+    tokens of its sequence."""
+    lens = [0, 1, 16, 17, 31, 32, 33, 50, 200]
+    if case.startswith("bf16"):
+        dim = int(case[-3:].lstrip("d"))
+        w = synth.WORKLOADS["varlen_16"]
+        make = lambda i, n: synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=3,
+                                                 head_dim=dim, seed=700 + i)
+    else:
+        dim = int(case[-3:].lstrip("d"))
+        make = lambda i, n: synth.prefill_inputs("tiny", seq_len=n, heads=3, head_dim=dim,
+                                                 init_std=0.02, seed=800 + i)
+    inp = packed_parts(lens, make)
+    T, H = inp["q"].shape[1], inp["q"].shape[2]
+    N = len(lens)
+    d_out, d_fin = loss_grads(inp, 13)
+    say("bwd checkpoints", case)
+    ws = torch.zeros(kda.bwd_workspace_size(T, N, H, dim), dtype=torch.uint8, device=DEV)
+    run_gpu(inp, d_out, d_fin, workspace=ws)
+    slots = f64(ws.view(torch.float32).reshape(-1, H, dim, dim))
+    flat = lambda x: f64(x.reshape(T, *x.shape[2:]))
+    st = seq_starts(inp)
+    _, _, snaps = oracle.kda_snapshots(flat(inp["q"]), flat(inp["k"]), flat(inp["v"]),
+                                       flat(inp["log_alpha"]), flat(inp["beta"]), 16,
+                                       state0=f64(inp["initial_state"]), seq_start=st)
+    s0 = f64(inp["initial_state"])
+    pairs, base = [], 0
+    for n in range(N):
+        L = st[n + 1] - st[n]
+        for j in range((L + 15) // 16):
+            ref = s0[n] if j == 0 else snaps[base + j - 1]
+            got = slots[st[n] // 16 + n + j]
+            pairs += [(got[h], ref[h]) for h in range(H)]
+        base += L // 16
+    err = max_rel_l2(pairs)
+    tol = TOL[inp["q"].dtype]
+    print(f"bwd checkpoints {case}: {len(pairs)} block states, max rel-L2 {err:.2e} (tol {tol})")
+    assert err <= tol
