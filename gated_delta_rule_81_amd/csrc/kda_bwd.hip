@@ -310,16 +310,6 @@ struct Prod<true> {
     }
 };
 
-// Four consecutive elements as fp32 (p 8-byte aligned for bf16, 16 for fp32).
-__device__ __forceinline__ f32x4 load4(const float *p) {
-    return *reinterpret_cast<const f32x4 *>(p);
-}
-__device__ __forceinline__ f32x4 load4(const bf16 *p) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-                 static_cast<float>(x[3])};
-}
-
 // Keeps the scheduler from hoisting the LDS reads of later products above
 // this point (which would hold their operands in registers early).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -331,7 +321,39 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-template <typename T, int D>
+// One thread's raw inputs of a chunk row piece: four elements as stored.
+template <typename T> struct RawIn;
+template <> struct RawIn<bf16> {
+    typedef u32x2 W;
+    W q, k, v, o;
+    f32x4 g;
+    float b;
+    __device__ static W ld(const bf16 *p) { return *reinterpret_cast<const W *>(p); }
+    __device__ static W zero() { return W{0u, 0u}; }
+    __device__ static f32x4 f32(const W &w) {
+        return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                     __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+    }
+};
+template <> struct RawIn<float> {
+    typedef f32x4 W;
+    W q, k, v, o;
+    f32x4 g;
+    float b;
+    __device__ static W ld(const float *p) { return *reinterpret_cast<const W *>(p); }
+    __device__ static W zero() { return zero4(); }
+    __device__ static f32x4 f32(const W &w) { return w; }
+};
+
+// BMODE (compile time): kBwdChain runs one workgroup per (sequence, head)
+// over the chunks in reverse and carries only dL/dS across them, writing the
+// gradient at every chunk's end to `dckpt` (and the initial-state gradient);
+// kBwdGrad runs one workgroup per (16-token slot, head) and forms every
+// other gradient of its chunk from the chunk's entering state (`ckpt`) and
+// end gradient (`dckpt`), independently of all other chunks.
+constexpr int kBwdChain = 1, kBwdGrad = 2;
+
+template <typename T, int D, int BMODE>
 __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -339,7 +361,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     const T *__restrict__ d_out, const float *__restrict__ d_final, T *__restrict__ dq,
     T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dlog_alpha,
     float *__restrict__ dbeta, float *__restrict__ d_initial, float *__restrict__ ckpt,
-    int seq_len, int total_tokens, int H, int states_ready) {
+    float *__restrict__ dckpt, int num_seqs, int seq_len, int total_tokens, int H,
+    int states_ready) {
     typedef BwdCfg<D> G;
     typedef Prod<sizeof(T) == 2> PR;  // bf16 inputs: bf16 products, fp32 accumulation
     constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
@@ -352,7 +375,29 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *sSD = sm + G::oSD;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
-    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    const int h = blockIdx.x % H;
+    // first token of sequence m (offsets clamped into [0, total_tokens])
+    auto seq_begin = [&](int m) -> int64_t {
+        if (!cu_seqlens) return (int64_t)m * seq_len;
+        const int a = cu_seqlens[m];
+        return a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+    };
+    int n, cfix = 0;
+    if constexpr (BMODE == kBwdGrad) {
+        // the slot's sequence: the last m whose first slot, begin(m) / 16 + m,
+        // is at or before it (bisection; ends for any offsets)
+        const int64_t slot = blockIdx.x / H;
+        int lo = 0, hi = num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seq_begin(mid) / kBC + mid <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        cfix = (int)(slot - (seq_begin(n) / kBC + n));
+    } else {
+        n = blockIdx.x / H;
+    }
     int64_t tbeg, tend;
     if (cu_seqlens) {
         int a = cu_seqlens[n], b = cu_seqlens[n + 1];
@@ -363,9 +408,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         tbeg = (int64_t)n * seq_len, tend = tbeg + seq_len;
     }
     const int nch = (int)((tend - tbeg + kBC - 1) / kBC);
+    // a slot between two sequences' chunks has no work
+    if (BMODE == kBwdGrad && (cfix < 0 || cfix >= nch)) return;
     const int64_t DD = (int64_t)D * D;
     // chunk c of this sequence keeps its entering state in slot tbeg / 16 + n + c
     float *ck = ckpt + ((tbeg / kBC + n) * H + h) * DD;
+    float *dck = dckpt + ((tbeg / kBC + n) * H + h) * DD;  // same slots, end gradients
     const int64_t ck_stride = (int64_t)H * DD;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
     const int vcol = 16 * w + r;  // S orientation: this lane's value column
@@ -373,26 +421,37 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
 
     // Stage chunk c: raw rows as fp32, the prefix G, K+, K-, Q+, Ke, gam, the
     // 16 x 16 matrices K+K-^T, A, M and T = (I + A)^-1 (and T^T).
-    auto prep = [&](int c, bool with_grad) -> int {
+    // Thread tid's raw inputs of chunk c: four consecutive channels of one row
+    // (16 x D = 4 x THREADS), kept as stored (bf16 bits or fp32) so that the
+    // loads can be in flight while other work runs; converted when staged.
+    // The forward pass (with_grad false) needs neither q nor d_out, the dL/dS
+    // chain no v.
+    auto raw_load = [&](int c, bool with_grad, bool with_v) -> RawIn<T> {
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
-        {  // thread tid: four consecutive channels of one row (16 x D = 4 x THREADS)
+        const int tok = tid / (D / 4), ch = 4 * (tid % (D / 4));
+        const bool ok = tok < nval;
+        const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
+        RawIn<T> R;
+        R.q = with_grad && ok ? RawIn<T>::ld(q + gi) : RawIn<T>::zero();
+        R.k = ok ? RawIn<T>::ld(k + gi) : RawIn<T>::zero();
+        R.v = with_v && ok ? RawIn<T>::ld(v + gi) : RawIn<T>::zero();
+        R.g = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + gi) : zero4();
+        R.o = with_grad && ok ? RawIn<T>::ld(d_out + gi) : RawIn<T>::zero();
+        R.b = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
+        return R;
+    };
+    auto prep = [&](int c, bool with_grad, const RawIn<T> &R) -> int {
+        const int64_t t0 = tbeg + (int64_t)c * kBC;
+        const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
+        {
             const int tok = tid / (D / 4), ch = 4 * (tid % (D / 4));
-            const bool ok = tok < nval;
-            const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
-            const f32x4 z = zero4();
-            // the forward pass (with_grad false) needs neither q nor d_out
-            const f32x4 rq = with_grad && ok ? load4(q + gi) : z, rk = ok ? load4(k + gi) : z;
-            const f32x4 rv = ok ? load4(v + gi) : z;
-            const f32x4 rg = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + gi) : z;
-            const f32x4 ro = with_grad && ok ? load4(d_out + gi) : z;
-            const float rb = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
-            if (with_grad) *reinterpret_cast<f32x4 *>(sQp + tok * LD + ch) = rq;
-            *reinterpret_cast<f32x4 *>(sKp + tok * LD + ch) = rk;
-            *reinterpret_cast<f32x4 *>(sV + tok * LD + ch) = rv;
-            *reinterpret_cast<f32x4 *>(sG + tok * LD + ch) = rg;
-            if (with_grad) *reinterpret_cast<f32x4 *>(sDO + tok * LD + ch) = ro;
-            if (tid < kBC) sBeta[tid] = rb;
+            if (with_grad) *reinterpret_cast<f32x4 *>(sQp + tok * LD + ch) = RawIn<T>::f32(R.q);
+            *reinterpret_cast<f32x4 *>(sKp + tok * LD + ch) = RawIn<T>::f32(R.k);
+            *reinterpret_cast<f32x4 *>(sV + tok * LD + ch) = RawIn<T>::f32(R.v);
+            *reinterpret_cast<f32x4 *>(sG + tok * LD + ch) = R.g;
+            if (with_grad) *reinterpret_cast<f32x4 *>(sDO + tok * LD + ch) = RawIn<T>::f32(R.o);
+            if (tid < kBC) sBeta[tid] = R.b;
         }
         __syncthreads();
         if (tid < D) {  // per channel prefix over the 16 rows
@@ -481,8 +540,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         Ss[t] = initial_state ? *reinterpret_cast<const f32x4 *>(
                                     initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * g4)
                               : zero4();
-    for (int c = 0; !states_ready && c < nch; ++c) {
-        prep(c, false);
+    for (int c = 0; BMODE == kBwdChain && !states_ready && c < nch; ++c) {
+        prep(c, false, raw_load(c, false, true));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4 *>(ck + c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4) =
@@ -510,55 +569,91 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     f32x4 dSs[NT];  // dL/dS at the chunk end, S orientation (value column vcol)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-        dSs[t] = d_final ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vcol * D +
-                                                            16 * t + 4 * g4)
-                         : zero4();
-    for (int c = nch - 1; c >= 0; --c) {
-        // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
-        // barriers separate these writes from those reads; the previous
-        // chunk's reads ended at its last barrier)
+        dSs[t] = BMODE == kBwdChain && d_final
+                     ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vcol * D +
+                                                        16 * t + 4 * g4)
+                     : zero4();
+    constexpr bool GRAD = BMODE == kBwdGrad, CHAIN = BMODE == kBwdChain;
+    // the chain prefetches chunk c - 1's rows while it works on chunk c
+    RawIn<T> nxt;
+    if (CHAIN && nch > 0) nxt = raw_load(nch - 1, true, false);
+    for (int c = GRAD ? cfix : nch - 1; c >= (GRAD ? cfix : 0); --c) {
+        RawIn<T> cur;
+        if constexpr (CHAIN) {
+            cur = nxt;
+            if (c > 0) nxt = raw_load(c - 1, true, false);
+        } else {
+            cur = raw_load(c, true, true);
+        }
+        if constexpr (CHAIN) {
+            // the chunk's end gradient for the gradient kernel
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4 *>(dck + c * ck_stride + (int64_t)vcol * D + 16 * t +
+                                           4 * g4) = dSs[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                dSs[t] = *reinterpret_cast<const f32x4 *>(dck + c * ck_stride +
+                                                          (int64_t)vcol * D + 16 * t + 4 * g4);
+        }
+        // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
+        // barriers separate these writes from those reads)
+#pragma unroll
+        for (int t = 0; t < NT && GRAD; ++t)
             *reinterpret_cast<f32x4 *>(sSD + vcol * G::LDSD + 16 * t + 4 * g4) = dSs[t];
         // the chunk's entering state in both orientations, loaded before the
         // staging so that the two sets of loads are in flight together
         const float *S0 = ck + c * ck_stride;
         f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT && GRAD; ++t) {
             Ss[t] = *reinterpret_cast<const f32x4 *>(S0 + (int64_t)vcol * D + 16 * t + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Sm[t][e] = S0[(int64_t)(16 * t + 4 * g4 + e) * D + kcol];
         }
-        const int nval = prep(c, true);
+        const int nval = prep(c, true, cur);
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
-        const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
-        f32x4 x, xb;
+        f32x4 x = zero4(), dl = zero4();
+        if constexpr (GRAD) {
+            const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
+            f32x4 xb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tok = 4 * g4 + e;
-            x[e] = sV[tok * LD + vcol] - pk[e];
-            xb[e] = sBeta[tok] * x[e];
+            for (int e = 0; e < 4; ++e) {
+                const int tok = 4 * g4 + e;
+                x[e] = sV[tok * LD + vcol] - pk[e];
+                xb[e] = sBeta[tok] * x[e];
+            }
+            dl = PR::lds_tile(zero4(), sT, LS, xb, lane);
+            sched_fence();
         }
-        const f32x4 dl = PR::lds_tile(zero4(), sT, LS, xb, lane);
-        sched_fence();
-        f32x4 ddl = PR::ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
-        ddl = PR::lds_reg(ddl, sKe, LD, dSs, lane);
+        // each product in its own accumulator: with bf16 operands the two are
+        // different MFMA shapes (16x16x16 and 16x16x32), and one's result fed
+        // straight in as the other's accumulator has produced wrong values in
+        // two of the four accumulator components when scheduled back to back
+        const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
+        const f32x4 dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
+        f32x4 ddl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + dde[e];
         sched_fence();
         const f32x4 lam = PR::lds_tile(zero4(), sTt, LS, ddl, lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             const float dx = sBeta[tok] * lam[e];
-            sDl[tok * LD + vcol] = dl[e];
-            sLm[tok * LD + vcol] = lam[e];
             sDX[tok * LD + vcol] = dx;
-            if (tok < nval) dv[((t0 + tok) * H + h) * (int64_t)D + vcol] = from_f32<T>(dx);
-            const float pb = row16_sum(x[e] * lam[e]);
-            if (r == 0) sDB[w * kBC + tok] = pb;
+            if constexpr (GRAD) {
+                sDl[tok * LD + vcol] = dl[e];
+                sLm[tok * LD + vcol] = lam[e];
+                if (tok < nval) dv[((t0 + tok) * H + h) * (int64_t)D + vcol] = from_f32<T>(dx);
+                const float pb = row16_sum(x[e] * lam[e]);
+                if (r == 0) sDB[w * kBC + tok] = pb;
+            }
         }
         __syncthreads();
+        if constexpr (GRAD) {
         if (w == 0) {  // dA, P = diag(b) dA and the K+K-^T part of db
             const f32x4 ld = PR::template lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
 #pragma unroll
@@ -585,8 +680,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             dbeta[(t0 + tid) * H + h] = s;
         }
         // key-column products (this wave's 16 key columns), with S0 in M orientation
-        const f32x4 dqp = PR::lds_lds(PR::lds_reg(zero4(), sDO, LD, Sm, lane), sDM, LS, sKm + 16 * w,
-                                     LD, lane);
+        // (separate accumulators for the two MFMA shapes, as for ddl above)
+        const f32x4 dqs = PR::lds_reg(zero4(), sDO, LD, Sm, lane);
+        const f32x4 dqm = PR::lds_lds(zero4(), sDM, LS, sKm + 16 * w, LD, lane);
+        f32x4 dqp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dqp[e] = dqs[e] + dqm[e];
         sched_fence();
         const f32x4 xs = PR::lds_reg(zero4(), sDX, LD, Sm, lane);
         sched_fence();
@@ -639,9 +738,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             if (tok < nval)
                 dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] = dgm[e] + above;
         }
+        }  // GRAD
         // state gradient before the chunk
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT && CHAIN; ++t) {
             const f32x4 u = PR::ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
             const f32x4 y = PR::ldst_lds(zero4(), sKp + 16 * t, LD, sDX + 16 * w, LD, lane);
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
@@ -649,9 +749,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
             sched_fence();
         }
-        __syncthreads();
+        if constexpr (CHAIN) __syncthreads();
     }
-    if (d_initial) {
+    if (CHAIN && d_initial) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             *reinterpret_cast<f32x4 *>(d_initial + sbase + (int64_t)vcol * D + 16 * t + 4 * g4) =
@@ -667,10 +767,11 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
                int seq_len, int total_tokens, int H, hipStream_t stream) {
     const int64_t units = (int64_t)num_seqs * H;
     if (units == 0) return 0;
-    if (units > (int64_t)1 << 30) return -1;
+    const int64_t slots = (int64_t)total_tokens / kBC + num_seqs + 1;
+    if (units > (int64_t)1 << 30 || slots * H > (int64_t)1 << 30) return -1;
     // The chunk-entering states from the prefill kernel (32-token chunks, all
     // CUs' worth of parallelism per head as in the forward) where it supports
-    // the configuration; otherwise pass 1 of this kernel recomputes them.
+    // the configuration; otherwise the chain kernel recomputes them first.
     int ready = 0;
     if ((sizeof(T) == 2 || D == 64) && (int64_t)H * D * 4 * 64 <= INT32_MAX) {
         if (launch_chunk_states(q, k, v, log_alpha, beta, initial_state, cu_seqlens, ckpt,
@@ -679,12 +780,18 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
             return -1;
         ready = 1;
     }
-    hipLaunchKernelGGL((chunk_bwd_kernel<T, D>), dim3((unsigned)units),
-                       dim3(BwdCfg<D>::THREADS), 0, stream, static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
-                       initial_state, cu_seqlens, static_cast<const T *>(d_out), d_final,
-                       static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv),
-                       dlog_alpha, dbeta, d_initial, ckpt, seq_len, total_tokens, H, ready);
+    float *dckpt = ckpt + slots * H * D * D;  // second region: chunk-end gradients
+#define KDA_BWD_KERNEL_ARGS                                                                    \
+    static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, \
+        beta, initial_state, cu_seqlens, static_cast<const T *>(d_out), d_final,              \
+        static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv), dlog_alpha, dbeta,   \
+        d_initial, ckpt, dckpt, num_seqs, seq_len, total_tokens, H, ready
+    hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChain>), dim3((unsigned)units),
+                       dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+    if (hipGetLastError() != hipSuccess) return -1;
+    hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdGrad>), dim3((unsigned)(slots * H)),
+                       dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+#undef KDA_BWD_KERNEL_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -692,7 +799,8 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
 
 int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
                                    int head_dim) {
-    return (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim;
+    // two regions of one state per slot and head: entering states, end gradients
+    return 2 * (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim;
 }
 
 int launch_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -224,11 +224,14 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  * chunkwise form ([Kimi-Linear], the section on KDA's per-channel forgetting:
  * training runs as matrix products instead of a token-serial RNN) but state
  * no gradient; this is the exact derivative of the recurrence of kda_chunk_fwd
- * (up to rounding), computed chunk by chunk (16 tokens) in reverse from each
- * chunk's entering state, which a forward pass in the same call writes to the
- * workspace first (bf16 at d 64 or 128 and fp32 at d 64: the prefill kernel
- * in a states-only mode, 32 tokens per step; fp32 at d 128: 16-token steps
- * inside the backward kernel).
+ * (up to rounding), per chunk of 16 tokens, in three launches on `stream`:
+ * (1) a forward pass writes every chunk's entering state to the workspace (bf16
+ * at d 64 or 128 and fp32 at d 64: the prefill kernel in a states-only mode,
+ * 32 tokens per step; fp32 at d 128: 16-token steps at the start of launch 2);
+ * (2) one workgroup per (sequence, head) carries dL/dS backwards over the
+ * chunks, which needs no forward state, and writes the gradient at every
+ * chunk's end to the workspace; (3) one workgroup per (chunk, head) forms all
+ * other gradients of its chunk from those two states.
  *
  * Inputs: q, k, v, log_alpha, beta, initial_state, cu_seqlens, batch, seq_len,
  * num_heads, head_dim_k, head_dim_v, num_seqs and dtype exactly as given to
@@ -242,8 +245,8 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  *   d_initial_state [N, H, d_v, d_k] fp32, or NULL (not written).
  * workspace: caller-owned device scratch, 16-byte aligned, of at least
  * kda_chunk_bwd_workspace_size(B * T, N, H, d_k) bytes (else KDA_ERR_SHAPE;
- * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state; contents
- * on return are unspecified.  No output may overlap an input, another output or
+ * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state and the
+ * gradient at its end; contents on return are unspecified.  No output may overlap an input, another output or
  * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
  * bf16 (bf16 inputs: bf16 matrix products with fp32 accumulation; fp32 inputs:
  * fp32 throughout).  Same numerics contract as
@@ -259,7 +262,7 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
 
 /*
  * Bytes of workspace kda_chunk_bwd needs for total_tokens = B * T tokens in
- * num_seqs sequences: (total_tokens / 16 + num_seqs + 1) * num_heads *
+ * num_seqs sequences: 2 * (total_tokens / 16 + num_seqs + 1) * num_heads *
  * head_dim^2 * 4.  -1 for negative sizes or head_dim not 64/128.  Host only.
  */
 int64_t kda_chunk_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs, int32_t num_heads,

@@ -299,8 +299,8 @@ def test_segmented_one_segment_needs_no_workspace():
 # ---------------------------------------------------------------- chunk_bwd
 def test_bwd_workspace_size():
     f = _lib.lib().kda_chunk_bwd_workspace_size
-    assert f(200, 2, 3, 128) == (200 // 16 + 2 + 1) * 3 * 128 * 128 * 4
-    assert f(0, 0, 3, 64) == 1 * 3 * 64 * 64 * 4
+    assert f(200, 2, 3, 128) == 2 * (200 // 16 + 2 + 1) * 3 * 128 * 128 * 4
+    assert f(0, 0, 3, 64) == 2 * 1 * 3 * 64 * 64 * 4
     for bad in [(-1, 1, 1, 64), (10, -1, 1, 64), (10, 1, -1, 64), (10, 1, 1, 96)]:
         assert f(*bad) == -1
 

@@ -203,7 +203,8 @@ def test_bwd_checkpoints_are_block_states(case):
     say("bwd checkpoints", case)
     ws = torch.zeros(kda.bwd_workspace_size(T, N, H, dim), dtype=torch.uint8, device=DEV)
     run_gpu(inp, d_out, d_fin, workspace=ws)
-    slots = f64(ws.view(torch.float32).reshape(-1, H, dim, dim))
+    # the first of the workspace's two regions: the entering states
+    slots = f64(ws.view(torch.float32).reshape(2, -1, H, dim, dim)[0])
     flat = lambda x: f64(x.reshape(T, *x.shape[2:]))
     st = seq_starts(inp)
     _, _, snaps = oracle.kda_snapshots(flat(inp["q"]), flat(inp["k"]), flat(inp["v"]),
