@@ -67,6 +67,10 @@ struct BwdCfg {
     // products that contract over d_v
     static constexpr int LDSD = D + 4, oSD = oDB + (W + 1) * kBC;
     static constexpr int FLOATS = oSD + D * LDSD;
+    // the chain kernel's transposed Q+ and K+ ([D][16], row stride LDT) share the
+    // space of the dL/dS copy, which only the gradient kernel uses
+    static constexpr int LDT = kBC + 4, oQT = oSD, oKT = oSD + D * LDT;
+    static_assert(2 * LDT <= LDSD, "transposed rows fit the dL/dS copy's space");
 };
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
@@ -373,6 +377,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *sM = sm + G::oM, *sT = sm + G::oT, *sTt = sm + G::oTt, *sP = sm + G::oP;
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
     float *sSD = sm + G::oSD;
+    float *sQT = sm + G::oQT, *sKT = sm + G::oKT;  // chain kernel only
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.x % H;
@@ -479,6 +484,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             sKm[tok * LD + ch] = kr / eg;
             sKe[tok * LD + ch] = kr * __expf(gl - gm);
             if (with_grad) sQp[tok * LD + ch] *= eg;
+            if (BMODE == kBwdChain && with_grad) {  // A operands of the dS products
+                sKT[ch * G::LDT + tok] = kr * eg;
+                sQT[ch * G::LDT + tok] = sQp[tok * LD + ch];
+            }
         }
         __syncthreads();
         if (w == 0) {
@@ -639,11 +648,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + dde[e];
         sched_fence();
         const f32x4 lam = PR::lds_tile(zero4(), sTt, LS, ddl, lane);
+        f32x4 dxr;  // dX in the accumulator layout: the B operand of K+^T dX
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             const float dx = sBeta[tok] * lam[e];
-            sDX[tok * LD + vcol] = dx;
+            dxr[e] = dx;
+            if constexpr (GRAD) sDX[tok * LD + vcol] = dx;
             if constexpr (GRAD) {
                 sDl[tok * LD + vcol] = dl[e];
                 sLm[tok * LD + vcol] = lam[e];
@@ -652,7 +663,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 if (r == 0) sDB[w * kBC + tok] = pb;
             }
         }
-        __syncthreads();
+        // (the chain's dS products below read only prep's LDS rows and registers)
+        if constexpr (GRAD) __syncthreads();
         if constexpr (GRAD) {
         if (w == 0) {  // dA, P = diag(b) dA and the K+K-^T part of db
             const f32x4 ld = PR::template lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
@@ -739,11 +751,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] = dgm[e] + above;
         }
         }  // GRAD
-        // state gradient before the chunk
+        // state gradient before the chunk: Q+^T dO and K+^T dX per key tile, A from
+        // the transposed rows, B (this wave's value columns) from registers
+        f32x4 dor;
+#pragma unroll
+        for (int e = 0; e < 4 && CHAIN; ++e) dor[e] = sDO[(4 * g4 + e) * LD + vcol];
 #pragma unroll
         for (int t = 0; t < NT && CHAIN; ++t) {
-            const f32x4 u = PR::ldst_lds(zero4(), sQp + 16 * t, LD, sDO + 16 * w, LD, lane);
-            const f32x4 y = PR::ldst_lds(zero4(), sKp + 16 * t, LD, sDX + 16 * w, LD, lane);
+            const f32x4 u = PR::lds_tile(zero4(), sQT + 16 * t * G::LDT, G::LDT, dor, lane);
+            const f32x4 y = PR::lds_tile(zero4(), sKT + 16 * t * G::LDT, G::LDT, dxr, lane);
             const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
