@@ -31,13 +31,21 @@
 // nothing.  16-token chunks keep e^(+-G) within fp32 under the library's
 // numerics contract (a 16-token gate sum above -80).
 //
-// One workgroup per (sequence, head), D / 16 waves.  Pass 1 runs the chunks
-// forward and writes each chunk's entering state to the workspace; pass 2 runs
-// them backward.  The states live in registers in two orientations: wave w
-// owns value columns 16w.. of S (for products that contract over d_k) and key
-// columns 16w.. of M = S^T (for products that contract over d_v), so no
-// product needs a cross-wave reduction.  Chunk operands are staged in LDS as
-// fp32.
+// The dS recursion, dS_prev = diag(gam) dS_C + Q+^T dO - K+^T dX, with dX =
+// diag(b) T^T (M^T dO + Ke dS_C), involves no forward state, so the work is
+// split over launches on one stream:
+//   1. every chunk's entering state S0 into the workspace (the prefill kernel's
+//      states mode; for fp32 at d = 128 the chain kernel's pass 1 instead);
+//   2. the chain kernel (kBwdChain), one workgroup per (sequence, head): the dS
+//      recursion over the chunks in reverse, dS_C of every chunk into the
+//      workspace's second region;
+//   3. the gradient kernel (kBwdGrad), one workgroup per (16-token slot, head):
+//      every other gradient of its chunk from its S0 and dS_C.
+// D / 16 waves per workgroup.  States are held in registers in two
+// orientations: wave w owns value columns 16w.. of S (for products that
+// contract over d_k) and key columns 16w.. of M = S^T (for products that
+// contract over d_v), so no product needs a cross-wave reduction.  Chunk
+// operands are staged in LDS as fp32.
 #include "kda_device.h"
 #include "kda_internal.h"
 
