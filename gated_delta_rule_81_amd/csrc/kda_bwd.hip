@@ -78,6 +78,8 @@ struct BwdCfg {
     // the chain kernel's transposed Q+ and K+ ([D][16], row stride LDT) share the
     // space of the dL/dS copy, which only the gradient kernel uses
     static constexpr int LDT = kBC + 4, oQT = oSD, oKT = oSD + D * LDT;
+    // A transposed (column m of A as a row), read by the triangular solve
+    static constexpr int oAt = FLOATS, FLOATS_ALL = oAt + SQ;
     static_assert(2 * LDT <= LDSD, "transposed rows fit the dL/dS copy's space");
 };
 
@@ -322,6 +324,14 @@ struct Prod<true> {
     }
 };
 
+// Every lane of a group of 4 receives x from lane SRC of its group (DPP
+// quad_perm, all lanes active).
+template <int SRC>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), SRC * 0x55, 0xf, 0xf, false));
+}
+
 // Keeps the scheduler from hoisting the LDS reads of later products above
 // this point (which would hold their operands in registers early).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -378,13 +388,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     typedef BwdCfg<D> G;
     typedef Prod<sizeof(T) == 2> PR;  // bf16 inputs: bf16 products, fp32 accumulation
     constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
-    __shared__ __attribute__((aligned(16))) float sm[G::FLOATS];
+    __shared__ __attribute__((aligned(16))) float sm[G::FLOATS_ALL];
     float *sQp = sm + G::oQp, *sKp = sm + G::oKp, *sKm = sm + G::oKm, *sKe = sm + G::oKe;
     float *sG = sm + G::oG, *sV = sm + G::oV, *sDO = sm + G::oDO, *sDl = sm + G::oDl;
-    float *sLm = sm + G::oLm, *sDX = sm + G::oDX, *sBr = sm + G::oBr, *sA = sm + G::oA;
+    float *sLm = sm + G::oLm, *sDX = sm + G::oDX, *sBr = sm + G::oBr;
     float *sM = sm + G::oM, *sT = sm + G::oT, *sTt = sm + G::oTt, *sP = sm + G::oP;
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
-    float *sSD = sm + G::oSD;
+    float *sSD = sm + G::oSD, *sAt = sm + G::oAt;
     float *sQT = sm + G::oQT, *sKT = sm + G::oKT;  // chain kernel only
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
@@ -504,37 +514,46 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
                 sBr[i * LS + r] = b[e];
-                sA[i * LS + r] = r < i ? sBeta[i] * b[e] : 0.f;
             }
-            // A is this wave's own LDS writes: a wave fence, no workgroup barrier
+            // A^T: lane (r, g) holds rows 4g .. 4g + 3 of column r of A
+            *reinterpret_cast<f32x4 *>(sAt + r * LS + 4 * g4) =
+                f32x4{4 * g4 > r ? sBeta[4 * g4] * b[0] : 0.f,
+                      4 * g4 + 1 > r ? sBeta[4 * g4 + 1] * b[1] : 0.f,
+                      4 * g4 + 2 > r ? sBeta[4 * g4 + 2] * b[2] : 0.f,
+                      4 * g4 + 3 > r ? sBeta[4 * g4 + 3] * b[3] : 0.f};
+            // A^T is this wave's own LDS writes: a wave fence, no workgroup barrier
             wave_lds_fence();
-            if (lane < kBC) {  // column j = lane of T by forward substitution
-                // j through an opaque move, so the identity's per-lane constants
-                // are formed here and not kept live across the kernel
-                int j;
-                asm volatile("v_mov_b32 %0, %1" : "=v"(j) : "v"(lane));
-                float col[kBC];
-                f32x4 nxt[4];  // row i + 1 of A, read while row i is solved
+            // T = (I + A)^{-1} by right-looking substitution: lane 4 j + q holds
+            // rows 4 q .. 4 q + 3 of column j; at step m the pivot T[m][j] comes
+            // from quad lane m / 4 and every row below it takes -A[row][m] x
+            {
+                const int j = lane >> 2, q = lane & 3;
+                float t[4];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = zero4();
+                for (int e = 0; e < 4; ++e) t[e] = (4 * q + e == j) ? 1.f : 0.f;
+                constexpr int LA = 4;  // columns of A read ahead of their step
+                f32x4 col[kBC - 1];
 #pragma unroll
-                for (int i = 0; i < kBC; ++i) {
-                    f32x4 cur[4];
+                for (int m = 0; m < LA; ++m)
+                    col[m] = *reinterpret_cast<const f32x4 *>(sAt + m * LS + 4 * q);
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
-                    if (i + 1 < kBC) {
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            nxt[q4] = *reinterpret_cast<const f32x4 *>(sA + (i + 1) * LS + 4 * q4);
+                for (int m = 0; m < kBC - 1; ++m) {
+                    if (m + LA < kBC - 1)
+                        col[m + LA] = *reinterpret_cast<const f32x4 *>(sAt + (m + LA) * LS + 4 * q);
+                    float x;
+                    switch (m >> 2) {
+                        case 0: x = quad_bcast<0>(t[m & 3]); break;
+                        case 1: x = quad_bcast<1>(t[m & 3]); break;
+                        case 2: x = quad_bcast<2>(t[m & 3]); break;
+                        default: x = quad_bcast<3>(t[m & 3]); break;
                     }
-                    float s = i == j ? 1.f : 0.f;
+                    // A[row][m] = 0 for row <= m: settled rows are unchanged
 #pragma unroll
-                    for (int m = 0; m < i; ++m) s -= cur[m / 4][m % 4] * col[m];
-                    col[i] = s;
-                    sT[i * LS + j] = s;
-                    sTt[j * LS + i] = s;
-                    sched_fence();
+                    for (int e = 0; e < 4; ++e) t[e] -= col[m][e] * x;
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sT[(4 * q + e) * LS + j] = t[e];
+                *reinterpret_cast<f32x4 *>(sTt + j * LS + 4 * q) = f32x4{t[0], t[1], t[2], t[3]};
             }
         } else if (w == 1 && with_grad) {
             const f32x4 m = PR::template lds_ldst<D>(zero4(), sQp, LD, sKm, LD, lane);
