@@ -27,6 +27,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--backward [--bwd-workload k3_prefill_32k|prefill_4k]]
                               (instead: kda_chunk_bwd, the gradients of the
                                prefill, on its own JSON line)
+       [--prefill-workload prefill_4k|varlen_16|k3_prefill_32k]
+                              (instead: kda_chunk_fwd alone on that workload, dense
+                               or packed; its own JSON line)
        [--segments G [--seg-workload long_1m|prefill_4k]]
                               (instead: kda_chunk_fwd_segmented with G requested
                                segments on one long sequence, kda_chunk_fwd
@@ -175,6 +178,67 @@ def bwd_bytes(T_tokens, H, d, n_seqs, esz=2):
     traffic the method adds, not algorithmic bytes."""
     per_token_head = (4 * d * esz + 4 * d + 4) + (3 * d * esz + 4 * d + 4)
     return T_tokens * H * per_token_head + 3 * n_seqs * H * d * d * 4
+
+
+def bench_prefill_workload(torch, args):
+    """kda_chunk_fwd alone on one named prefill workload (dense or packed;
+    inputs seeded and resident in HBM), timed with HIP events."""
+    import synth
+    import gated_delta_rule_81_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.prefill_workload]
+    log("generating", w.notes)
+    inp = synth.prefill_inputs(w)
+    P = {key: inp[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
+    s0 = inp["initial_state"]
+    s0 = None if s0 is None else s0.to(dev)
+    cu = inp.get("cu_seqlens")
+    cu = None if cu is None else cu.to(dev)
+    B, T, H, D = P["q"].shape
+    n_seqs = (cu.numel() - 1) if cu is not None else B
+    out = torch.empty_like(P["v"])
+    fin = torch.empty((n_seqs, H, D, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], s0, cu, out=out,
+                      final_state=fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    log(f"timing {K} x kda_chunk_fwd on {w.name}")
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(K):
+        step()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
+    avg = sum(ms) / K
+    tokens = B * T
+    nbytes = prefill_bytes(tokens, H, D, n_seqs, esz=P["q"].element_size())
+    if s0 is None:  # no initial state is read
+        nbytes -= n_seqs * H * D * D * 4
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    log(f"kda_chunk_fwd on {w.name}: avg {avg:.3f} ms (min {min(ms):.3f})")
+    return {"metric": f"KDA chunked-fwd tokens/s ({w.name})", "value": tokens / (avg * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+            "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if P["q"].dtype == torch.bfloat16 else "f32",
+            "data": "synthetic",
+            "config": {"workload": f"kda_chunk_fwd {w.name}: {w.notes}", "tokens": tokens,
+                       "sequences": n_seqs, "heads": H, "head_dim": D},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "kernel_ms_avg": avg, "kernel_ms_min": min(ms), "algorithmic_bytes": nbytes,
+            "cpu_baseline": None}
 
 
 def bench_backward(torch, args):
@@ -358,6 +422,9 @@ def main():
     ap.add_argument("--bwd-workload", default="k3_prefill_32k",
                     choices=["k3_prefill_32k", "prefill_4k"],
                     help="the prefill workload --backward runs on")
+    ap.add_argument("--prefill-workload", default=None,
+                    choices=["prefill_4k", "varlen_16", "k3_prefill_32k"],
+                    help="time kda_chunk_fwd alone on this workload instead (its own JSON line)")
     args = ap.parse_args()
     if args.scalar_gate and args.snapshot_every:
         ap.error("--scalar-gate and --snapshot-every time different entry points; pick one")
@@ -376,6 +443,9 @@ def main():
         return
     if args.backward:
         print(json.dumps(bench_backward(torch, args)), flush=True)
+        return
+    if args.prefill_workload:
+        print(json.dumps(bench_prefill_workload(torch, args)), flush=True)
         return
 
     import synth

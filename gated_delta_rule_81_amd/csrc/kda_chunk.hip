@@ -410,7 +410,9 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
 //               with e^{Gamma_15} S + (K e^{Gamma_15 - Gamma})_{0..15}^T Delta_0,
 //               the block-0 half of the chunk's own transition.
 constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
-template <typename T, int D, int DVS, bool SG, int MODE>
+// LPT (compile time, packed input with at most 64 sequences): workgroups take
+// the sequences longest first (see below); otherwise in sequence order.
+template <typename T, int D, int DVS, bool SG, int MODE, bool LPT>
 __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -429,7 +431,32 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     // so give each XCD a contiguous run of units; the NS slices of one
     // (sequence, head) then share that XCD's L2 for their common inputs.
     const int bid = blockIdx.x;
-    const int unit = (bid & 7) * units_per_xcd + (bid >> 3);
+    int unit = (bid & 7) * units_per_xcd + (bid >> 3);
+    if constexpr (LPT) {
+        // Packed sequences of unequal length: longest first, so the longest
+        // chains start at once and shorter ones fill in behind them.  The k-th
+        // workgroup dispatched to XCD x takes position u of the longest-first
+        // order; the NS slices of a head stay together on one XCD and heads go
+        // round-robin over the XCDs.  (The grid is padded to 8 NS units.)
+        const int lane = threadIdx.x & 63, k = bid >> 3;
+        const int u = NS * (8 * (k / NS) + (bid & 7)) + k % NS;
+        int len = -1;  // lane m: the clamped length of sequence m
+        if (lane < num_seqs) {
+            int a = cu_seqlens[lane], b = cu_seqlens[lane + 1];
+            a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+            b = b < a ? a : (b > total_tokens ? total_tokens : b);
+            len = b - a;
+        }
+        int rank = 0;  // longer sequences, then equal ones with a smaller index
+        for (int m = 0; m < num_seqs; ++m) {
+            const int lm = __builtin_amdgcn_readlane(len, m);
+            rank += (lm > len || (lm == len && m < lane)) ? 1 : 0;
+        }
+        const int p = u / (H * NS);
+        const unsigned long long hit = __ballot(lane < num_seqs && rank == p);
+        const int m = hit ? __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1) : num_seqs;
+        unit = m * H * NS + u % (H * NS);
+    }
     if (unit >= units) return;
     const int slice = unit % NS;
     const int nh = unit / NS;
@@ -970,12 +997,20 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
     if (units64 == 0) return 0;
     if (units64 > (int64_t)1 << 30) return -1;
     const int units = (int)units64;
-    const int per_xcd = (units + 7) / 8;
-    hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE>), dim3(8 * per_xcd),
-                       dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v), log_alpha, beta,
-                       initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,
-                       snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd);
+    // a multiple of the slices per head, so that the longest-first order of
+    // packed sequences maps the grid onto every unit
+    const int per_xcd = (units + 8 * (D / DVS) - 1) / (8 * (D / DVS)) * (D / DVS);
+#define KDA_KERNEL_ARGS                                                                        \
+    static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), log_alpha,  \
+        beta, initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,        \
+        snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd
+    if (cu_seqlens && num_seqs <= 64)  // packed: longest sequences first
+        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, true>), dim3(8 * per_xcd),
+                           dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, KDA_KERNEL_ARGS);
+    else
+        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, false>), dim3(8 * per_xcd),
+                           dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, KDA_KERNEL_ARGS);
+#undef KDA_KERNEL_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
