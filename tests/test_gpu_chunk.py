@@ -137,6 +137,37 @@ def test_varlen_equals_separate_runs_and_is_deterministic():
         off += lens[i]
 
 
+def test_varlen_dispatch_orders_agree():
+    """Packed input takes sequences longest first when there are at most 64 of
+    them and in sequence order otherwise: 80 short sequences (sequence order)
+    against the oracle, and their first 64 packed alone (longest first) equal
+    bitwise to the same sequences of the 80-sequence run."""
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(0, 120, size=80)]
+    lens[3] = 0
+    lens[10] = 500  # one long sequence among short ones
+    w = synth.WORKLOADS["varlen_16"]
+    parts = [synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=2, head_dim=64, seed=900 + i)
+             for i, n in enumerate(lens)]
+
+    def pack(ps, ls):
+        cat = lambda key: torch.cat([p[key] for p in ps], dim=1)
+        inp = {key: cat(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+        inp["initial_state"] = torch.cat([p["initial_state"] for p in ps])
+        inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(ls)]),
+                                         dtype=torch.int32)
+        return inp
+
+    say("varlen dispatch orders", len(lens), "and 64 sequences")
+    inp80, inp64 = pack(parts, lens), pack(parts[:64], lens[:64])
+    out80, fin80 = run(inp80)
+    out64, fin64 = run(inp64)
+    check(inp80, out80, fin80, label="varlen 80 sequences")
+    t64 = int(np.sum(lens[:64]))
+    assert torch.equal(out64[0], out80[0, :t64])
+    assert torch.equal(fin64, fin80[:64])
+
+
 def test_no_initial_state_equals_zeros_and_no_final_state():
     inp = synth.prefill_inputs("prefill_4k", seq_len=90, heads=2)
     say("null states")
