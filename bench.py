@@ -24,7 +24,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                                scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
        [--skip-decode]        (decode workload shrunk to one session-head; for
                                counter passes on kda_chunk_fwd only)
-       [--backward [--bwd-workload k3_prefill_32k|prefill_4k]]
+       [--backward [--bwd-workload k3_prefill_32k|prefill_4k|varlen_16]]
                               (instead: kda_chunk_bwd, the gradients of the
                                prefill, on its own JSON line)
        [--prefill-workload prefill_4k|varlen_16|k3_prefill_32k]
@@ -255,18 +255,22 @@ def bench_backward(torch, args):
     P = {key: inp[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
     s0 = inp["initial_state"]
     s0 = None if s0 is None else s0.to(dev)
+    cu = inp.get("cu_seqlens")
+    cu = None if cu is None else cu.to(dev)
     gen = torch.Generator().manual_seed(w.seed + 100)
-    T, H, D = w.seq_len * w.batch, w.heads, w.head_dim
-    d_out = torch.randn(w.batch, w.seq_len, H, D, generator=gen).to(P["q"].dtype).to(dev)
-    d_fin = (torch.randn(w.batch, H, D, D, generator=gen) * 0.1).to(dev)
-    ws = torch.empty(kda.bwd_workspace_size(T, w.batch, H, D), dtype=torch.uint8, device=dev)
-    grads = kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0,
+    Bq, Tq, H, D = P["q"].shape
+    T = Bq * Tq
+    n_seqs = (cu.numel() - 1) if cu is not None else Bq
+    d_out = torch.randn(Bq, Tq, H, D, generator=gen).to(P["q"].dtype).to(dev)
+    d_fin = (torch.randn(n_seqs, H, D, D, generator=gen) * 0.1).to(dev)
+    ws = torch.empty(kda.bwd_workspace_size(T, n_seqs, H, D), dtype=torch.uint8, device=dev)
+    grads = kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0, cu,
                           workspace=ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0,
+        kda.chunk_bwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], d_out, d_fin, s0, cu,
                       workspace=ws, grads=grads)
 
     for _ in range(args.warmup):
@@ -285,7 +289,7 @@ def bench_backward(torch, args):
     ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
     avg = sum(ms) / K
     log(f"kda_chunk_bwd: avg {avg:.3f} ms (min {min(ms):.3f})")
-    nbytes = bwd_bytes(T, H, D, w.batch)
+    nbytes = bwd_bytes(T, H, D, n_seqs)
     gbs = nbytes / (avg * 1e-3) / 1e9
     # per token-head, in multiply-adds: the forward recompute (K+ S0 and
     # Ke^T Delta: 2 d^2) and the gradient pass (K+ S0, Ke dS, dO S0^T,
@@ -314,7 +318,8 @@ def bench_backward(torch, args):
         "data": "synthetic",
         "config": {"workload": f"kda_chunk_bwd {w.name}: {w.notes}; "
                                + ("bf16 products, fp32 accumulation" if bf else "fp32 products")
-                               + ", 16-token chunks", "tokens": T, "heads": H, "head_dim": D},
+                               + ", 16-token chunks", "tokens": T, "sequences": n_seqs,
+                   "heads": H, "head_dim": D},
         "roofline": roof,
         "kernel_ms_avg": avg, "kernel_ms_min": min(ms), "algorithmic_bytes": nbytes,
         "flop_per_launch": flop,
@@ -420,7 +425,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time kda_chunk_bwd (the prefill's gradients) instead")
     ap.add_argument("--bwd-workload", default="k3_prefill_32k",
-                    choices=["k3_prefill_32k", "prefill_4k"],
+                    choices=["k3_prefill_32k", "prefill_4k", "varlen_16"],
                     help="the prefill workload --backward runs on")
     ap.add_argument("--prefill-workload", default=None,
                     choices=["prefill_4k", "varlen_16", "k3_prefill_32k"],

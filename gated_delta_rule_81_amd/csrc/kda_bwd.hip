@@ -420,6 +420,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         cfix = (int)(slot - (seq_begin(n) / kBC + n));
     } else {
         n = blockIdx.x / H;
+        if (cu_seqlens && num_seqs <= 64) {
+            // packed: the chains of the longest sequences go first (workgroups
+            // are dispatched in index order); lane m ranks sequence m by its
+            // clamped length, ties by index
+            const int lane = tid & 63;
+            int len = -1;
+            if (lane < num_seqs) {
+                int a = cu_seqlens[lane], b = cu_seqlens[lane + 1];
+                a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+                b = b < a ? a : (b > total_tokens ? total_tokens : b);
+                len = b - a;
+            }
+            int rank = 0;
+            for (int m = 0; m < num_seqs; ++m) {
+                const int lm = __builtin_amdgcn_readlane(len, m);
+                rank += (lm > len || (lm == len && m < lane)) ? 1 : 0;
+            }
+            const unsigned long long hit = __ballot(lane < num_seqs && rank == n);
+            n = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+        }
     }
     int64_t tbeg, tend;
     if (cu_seqlens) {
