@@ -332,6 +332,40 @@ __device__ __forceinline__ float quad_bcast(float x) {
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), SRC * 0x55, 0xf, 0xf, false));
 }
 
+// Chunk-entering states in the workspace's first region are kept in the
+// input dtype: bf16 for bf16 inputs, whose matrix products read them as bf16
+// operands anyway (only the fp32 row sum behind dG_last sees the rounding).
+// `base` points at a slot of that region; offsets count elements.
+template <typename T>
+__device__ __forceinline__ void ckpt_store(float *base, int64_t off, const f32x4 &x) {
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = static_cast<bf16>(x[e]);
+        *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(base) + off) = h;
+    } else {
+        *reinterpret_cast<f32x4 *>(base + off) = x;
+    }
+}
+template <typename T>
+__device__ __forceinline__ f32x4 ckpt_load4(const float *base, int64_t off) {
+    if constexpr (sizeof(T) == 2) {
+        const bf16x4 h =
+            *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(base) + off);
+        return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]),
+                     static_cast<float>(h[2]), static_cast<float>(h[3])};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(base + off);
+    }
+}
+template <typename T>
+__device__ __forceinline__ float ckpt_load1(const float *base, int64_t off) {
+    if constexpr (sizeof(T) == 2)
+        return static_cast<float>(reinterpret_cast<const bf16 *>(base)[off]);
+    else
+        return base[off];
+}
+
 // Keeps the scheduler from hoisting the LDS reads of later products above
 // this point (which would hold their operands in registers early).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -455,7 +489,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     if (BMODE == kBwdGrad && (cfix < 0 || cfix >= nch)) return;
     const int64_t DD = (int64_t)D * D;
     // chunk c of this sequence keeps its entering state in slot tbeg / 16 + n + c
-    float *ck = ckpt + ((tbeg / kBC + n) * H + h) * DD;
+    // this sequence's first checkpoint slot, counted in elements of T
+    float *ck = sizeof(T) == 2
+                    ? reinterpret_cast<float *>(reinterpret_cast<bf16 *>(ckpt) +
+                                                ((tbeg / kBC + n) * H + h) * DD)
+                    : ckpt + ((tbeg / kBC + n) * H + h) * DD;
     float *dck = dckpt + ((tbeg / kBC + n) * H + h) * DD;  // same slots, end gradients
     const int64_t ck_stride = (int64_t)H * DD;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
@@ -600,8 +638,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         prep(c, false, raw_load(c, false, true));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4 *>(ck + c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4) =
-                Ss[t];
+            ckpt_store<T>(ck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4, Ss[t]);
         const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
         f32x4 xb;
 #pragma unroll
@@ -660,13 +697,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             *reinterpret_cast<f32x4 *>(sSD + vcol * G::LDSD + 16 * t + 4 * g4) = dSs[t];
         // the chunk's entering state in both orientations, loaded before the
         // staging so that the two sets of loads are in flight together
-        const float *S0 = ck + c * ck_stride;
+        const int64_t s0 = c * ck_stride;  // element offset of S0 in the checkpoints
         f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
 #pragma unroll
         for (int t = 0; t < NT && GRAD; ++t) {
-            Ss[t] = *reinterpret_cast<const f32x4 *>(S0 + (int64_t)vcol * D + 16 * t + 4 * g4);
+            Ss[t] = ckpt_load4<T>(ck, s0 + (int64_t)vcol * D + 16 * t + 4 * g4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Sm[t][e] = S0[(int64_t)(16 * t + 4 * g4 + e) * D + kcol];
+            for (int e = 0; e < 4; ++e)
+                Sm[t][e] = ckpt_load1<T>(ck, s0 + (int64_t)(16 * t + 4 * g4 + e) * D + kcol);
         }
         const int nval = prep(c, true, cur);
         const int64_t t0 = tbeg + (int64_t)c * kBC;

@@ -406,7 +406,8 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
 //   kModeStates no outputs: the state entering every 16-token block of each
 //               sequence (the checkpoints of the chunked backward) goes to
 //               `snapshots`, slot tbeg / 16 + n + j for block j of sequence n,
-//               [slot][H][d_v][d_k].  A 32-token chunk's second block enters
+//               [slot][H][d_v][d_k] in the input dtype (bf16 for bf16 inputs).
+//               A 32-token chunk's second block enters
 //               with e^{Gamma_15} S + (K e^{Gamma_15 - Gamma})_{0..15}^T Delta_0,
 //               the block-0 half of the chunk's own transition.
 constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
@@ -936,12 +937,21 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 const typename SM::Frag Dbm = SM::b(Dl[0], zero4());
                 const float *cRho =
                     reinterpret_cast<const float *>(smem + G::oO) + ((tick - 1) & 1) * D;
-                float *dst = snapshots + ((tbeg / kBS + n + m2) * H + h) * (int64_t)D * D +
-                             (int64_t)vcol * D + 4 * l4;
+                // element offset of this lane's four rows; the states are kept in
+                // the input dtype (bf16 for bf16 inputs)
+                const int64_t off = ((tbeg / kBS + n + m2) * H + h) * (int64_t)D * D +
+                                    (int64_t)vcol * D + 4 * l4;
                 const int64_t blk = (int64_t)H * D * D;
+                auto put = [&](int64_t e0, const f32x4 &x) {
+                    if constexpr (sizeof(T) == 2)
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16 *>(snapshots) + e0) =
+                            u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+                    else
+                        *reinterpret_cast<f32x4 *>(snapshots + e0) = x;
+                };
 #pragma unroll
                 for (int t = 0; t < G::NRT; ++t) {
-                    *reinterpret_cast<f32x4 *>(dst + 16 * t) = Sm[t];
+                    put(off + 16 * t, Sm[t]);
                     if (mid) {
                         const f32x4 acc =
                             SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Dbm);
@@ -949,7 +959,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                         f32x4 sm;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) sm[e] = rh[e] * Sm[t][e] + acc[e];
-                        *reinterpret_cast<f32x4 *>(dst + blk + 16 * t) = sm;
+                        put(off + blk + 16 * t, sm);
                     }
                 }
             }

@@ -180,7 +180,7 @@ def packed_parts(lens, make):
 def test_bwd_checkpoints_are_block_states(case):
     """White-box: on return the workspace holds the state entering every
     16-token block of every sequence (slot t0 // 16 + n + j for block j of
-    sequence n starting at token t0, [slot][H][d_v][d_k]).  For bf16 and for
+    sequence n starting at token t0, [slot][H][d_v][d_k], in the input dtype).  For bf16 and for
     fp32 at d = 64 the prefill kernel's states mode writes them (32-token chunks:
     even blocks are chunk-entering states, odd blocks the state after a chunk's
     first 16 tokens); fp32 at d = 128 recomputes them inside the backward
@@ -203,8 +203,8 @@ def test_bwd_checkpoints_are_block_states(case):
     say("bwd checkpoints", case)
     ws = torch.zeros(kda.bwd_workspace_size(T, N, H, dim), dtype=torch.uint8, device=DEV)
     run_gpu(inp, d_out, d_fin, workspace=ws)
-    # the first of the workspace's two regions: the entering states
-    slots = f64(ws.view(torch.float32).reshape(2, -1, H, dim, dim)[0])
+    n_slots = T // 16 + N + 1  # the first region: states in the input dtype
+    slots = f64(ws.view(inp["q"].dtype)[:n_slots * H * dim * dim].reshape(n_slots, H, dim, dim))
     flat = lambda x: f64(x.reshape(T, *x.shape[2:]))
     st = seq_starts(inp)
     _, _, snaps = oracle.kda_snapshots(flat(inp["q"]), flat(inp["k"]), flat(inp["v"]),
