@@ -332,10 +332,11 @@ __device__ __forceinline__ float quad_bcast(float x) {
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), SRC * 0x55, 0xf, 0xf, false));
 }
 
-// Chunk-entering states in the workspace's first region are kept in the
-// input dtype: bf16 for bf16 inputs, whose matrix products read them as bf16
-// operands anyway (only the fp32 row sum behind dG_last sees the rounding).
-// `base` points at a slot of that region; offsets count elements.
+// The workspace's checkpoints (chunk-entering states in the first region,
+// chunk-end gradients in the second) are kept in the input dtype: bf16 for
+// bf16 inputs, whose matrix products read them as bf16 operands anyway (only
+// the fp32 row sums behind dG_last see the rounding).  `base` points at a
+// slot of a region; offsets count elements.
 template <typename T>
 __device__ __forceinline__ void ckpt_store(float *base, int64_t off, const f32x4 &x) {
     if constexpr (sizeof(T) == 2) {
@@ -494,7 +495,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                     ? reinterpret_cast<float *>(reinterpret_cast<bf16 *>(ckpt) +
                                                 ((tbeg / kBC + n) * H + h) * DD)
                     : ckpt + ((tbeg / kBC + n) * H + h) * DD;
-    float *dck = dckpt + ((tbeg / kBC + n) * H + h) * DD;  // same slots, end gradients
+    float *dck = sizeof(T) == 2  // same slots, end gradients
+                     ? reinterpret_cast<float *>(reinterpret_cast<bf16 *>(dckpt) +
+                                                 ((tbeg / kBC + n) * H + h) * DD)
+                     : dckpt + ((tbeg / kBC + n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
     const int vcol = 16 * w + r;  // S orientation: this lane's value column
@@ -682,13 +686,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             // the chunk's end gradient for the gradient kernel
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                *reinterpret_cast<f32x4 *>(dck + c * ck_stride + (int64_t)vcol * D + 16 * t +
-                                           4 * g4) = dSs[t];
+                ckpt_store<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4, dSs[t]);
         } else {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                dSs[t] = *reinterpret_cast<const f32x4 *>(dck + c * ck_stride +
-                                                          (int64_t)vcol * D + 16 * t + 4 * g4);
+                dSs[t] = ckpt_load4<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4);
         }
         // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
         // barriers separate these writes from those reads)

@@ -245,8 +245,8 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  *   d_initial_state [N, H, d_v, d_k] fp32, or NULL (not written).
  * workspace: caller-owned device scratch, 16-byte aligned, of at least
  * kda_chunk_bwd_workspace_size(B * T, N, H, d_k) bytes (else KDA_ERR_SHAPE;
- * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state (in the
- * input dtype) and the gradient at its end (fp32); contents on return are
+ * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state and the
+ * gradient at its end (both in the input dtype); contents on return are
  * unspecified.  No output may overlap an input, another output or
  * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
  * bf16 (bf16 inputs: bf16 matrix products with fp32 accumulation; fp32 inputs:
