@@ -36,9 +36,10 @@
 // split over launches on one stream:
 //   1. every chunk's entering state S0 into the workspace (the prefill kernel's
 //      states mode; for fp32 at d = 128 the chain kernel's pass 1 instead);
-//   2. the chain kernel (kBwdChain), one workgroup per (sequence, head): the dS
-//      recursion over the chunks in reverse, dS_C of every chunk into the
-//      workspace's second region;
+//   2. the chain kernel, two workgroups per (sequence, head), one per half of
+//      the value columns (kBwdChainHalf; kBwdChain, one workgroup per head,
+//      where pass 1 runs in it): the dS recursion over the chunks in reverse,
+//      dS_C of every chunk into the workspace's second region;
 //   3. the gradient kernel (kBwdGrad), one workgroup per (16-token slot, head):
 //      every other gradient of its chunk from its S0 and dS_C.
 // D / 16 waves per workgroup.  States are held in registers in two
@@ -81,6 +82,10 @@ struct BwdCfg {
     // A transposed (column m of A as a row), read by the triangular solve
     static constexpr int oAt = FLOATS, FLOATS_ALL = oAt + SQ;
     static_assert(2 * LDT <= LDSD, "transposed rows fit the dL/dS copy's space");
+    // the half-column chain's partial K_end dS tiles (one f32x4 per lane and
+    // wave), after the transposed rows
+    static constexpr int oXC = oKT + D * LDT;
+    static_assert(oXC + W * 64 * 4 <= oSD + D * LDSD, "exchange fits the dL/dS copy's space");
 };
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
@@ -405,10 +410,14 @@ template <> struct RawIn<float> {
 // BMODE (compile time): kBwdChain runs one workgroup per (sequence, head)
 // over the chunks in reverse and carries only dL/dS across them, writing the
 // gradient at every chunk's end to `dckpt` (and the initial-state gradient);
+// kBwdChainHalf does the same with two workgroups per (sequence, head), each
+// owning half of the value columns (the columns of dL/dS evolve independently):
+// its wave w holds 16 value columns for half of the key tiles, so the one
+// product that contracts over d_k (K_end dS) sums two waves' halves in LDS;
 // kBwdGrad runs one workgroup per (16-token slot, head) and forms every
 // other gradient of its chunk from the chunk's entering state (`ckpt`) and
 // end gradient (`dckpt`), independently of all other chunks.
-constexpr int kBwdChain = 1, kBwdGrad = 2;
+constexpr int kBwdChain = 1, kBwdGrad = 2, kBwdChainHalf = 3;
 
 template <typename T, int D, int BMODE>
 __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
@@ -431,9 +440,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
     float *sSD = sm + G::oSD, *sAt = sm + G::oAt;
     float *sQT = sm + G::oQT, *sKT = sm + G::oKT;  // chain kernel only
+    constexpr bool HALF = BMODE == kBwdChainHalf;
+    // the half-column chain: key tiles per wave, and this wave's half of them
+    constexpr int NTW = HALF ? NT / 2 : NT;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.x % H;
+    const int kh = HALF ? w / (G::W / 2) : 0;
+    const int vhalf = HALF ? (int)((blockIdx.x / H) & 1) : 0;
     // first token of sequence m (offsets clamped into [0, total_tokens])
     auto seq_begin = [&](int m) -> int64_t {
         if (!cu_seqlens) return (int64_t)m * seq_len;
@@ -454,7 +468,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         n = lo;
         cfix = (int)(slot - (seq_begin(n) / kBC + n));
     } else {
-        n = blockIdx.x / H;
+        n = HALF ? (int)(blockIdx.x / H >> 1) : (int)(blockIdx.x / H);
         if (cu_seqlens && num_seqs <= 64) {
             // packed: the chains of the longest sequences go first (workgroups
             // are dispatched in index order); lane m ranks sequence m by its
@@ -501,7 +515,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                      : dckpt + ((tbeg / kBC + n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
-    const int vcol = 16 * w + r;  // S orientation: this lane's value column
+    // S orientation: this lane's value column (the half-column chain: wave
+    // w % (W / 2) of value half vhalf)
+    const int vcol = HALF ? D / 2 * vhalf + 16 * (w % (G::W / 2)) + r : 16 * w + r;
     const int kcol = 16 * w + r;  // M orientation: this lane's key column
 
     // Stage chunk c: raw rows as fp32, the prefix G, K+, K-, Q+, Ke, gam, the
@@ -564,7 +580,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             sKm[tok * LD + ch] = kr / eg;
             sKe[tok * LD + ch] = kr * __expf(gl - gm);
             if (with_grad) sQp[tok * LD + ch] *= eg;
-            if (BMODE == kBwdChain && with_grad) {  // A operands of the dS products
+            if (BMODE != kBwdGrad && with_grad) {  // A operands of the dS products
                 sKT[ch * G::LDT + tok] = kr * eg;
                 sQT[ch * G::LDT + tok] = sQp[tok * LD + ch];
             }
@@ -663,14 +679,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     }
 
     // ------------------------------------------------------------ pass 2
-    f32x4 dSs[NT];  // dL/dS at the chunk end, S orientation (value column vcol)
+    // dL/dS at the chunk end, S orientation (value column vcol; key tiles
+    // kh * NTW + t)
+    f32x4 dSs[NTW];
+    constexpr bool GRAD = BMODE == kBwdGrad, CHAIN = !GRAD;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        dSs[t] = BMODE == kBwdChain && d_final
+    for (int t = 0; t < NTW; ++t)
+        dSs[t] = CHAIN && d_final
                      ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vcol * D +
-                                                        16 * t + 4 * g4)
+                                                        16 * (kh * NTW + t) + 4 * g4)
                      : zero4();
-    constexpr bool GRAD = BMODE == kBwdGrad, CHAIN = BMODE == kBwdChain;
     // the chain prefetches chunk c - 1's rows while it works on chunk c
     RawIn<T> nxt;
     if (CHAIN && nch > 0) nxt = raw_load(nch - 1, true, false);
@@ -685,8 +703,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         if constexpr (CHAIN) {
             // the chunk's end gradient for the gradient kernel
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                ckpt_store<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4, dSs[t]);
+            for (int t = 0; t < NTW; ++t)
+                ckpt_store<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * (kh * NTW + t) + 4 * g4,
+                              dSs[t]);
         } else {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
@@ -695,7 +714,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
         // barriers separate these writes from those reads)
 #pragma unroll
-        for (int t = 0; t < NT && GRAD; ++t)
+        for (int t = 0; t < NTW && GRAD; ++t)
             *reinterpret_cast<f32x4 *>(sSD + vcol * G::LDSD + 16 * t + 4 * g4) = dSs[t];
         // the chunk's entering state in both orientations, loaded before the
         // staging so that the two sets of loads are in flight together
@@ -728,11 +747,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // different MFMA shapes (16x16x16 and 16x16x32), and one's result fed
         // straight in as the other's accumulator has produced wrong values in
         // two of the four accumulator components when scheduled back to back
-        const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + 16 * w, LD, lane);
-        const f32x4 dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
+        const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + (vcol - r), LD, lane);
+        const f32x4 dde = PR::lds_reg(zero4(), sKe + 16 * NTW * kh, LD, dSs, lane);
         f32x4 ddl;
+        if constexpr (HALF) {
+            // the other key half's partial from the partner wave (same value
+            // columns), summed in one order in both waves
+            f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
+            sx[w * 64 + lane] = dde;
+            __syncthreads();
+            const f32x4 o = sx[(w ^ (G::W / 2)) * 64 + lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + dde[e];
+            for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + (kh == 0 ? dde[e] + o[e] : o[e] + dde[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + dde[e];
+        }
         sched_fence();
         const f32x4 lam = PR::lds_tile(zero4(), sTt, LS, ddl, lane);
         f32x4 dxr;  // dX in the accumulator layout: the B operand of K+^T dX
@@ -844,10 +874,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
 #pragma unroll
         for (int e = 0; e < 4 && CHAIN; ++e) dor[e] = sDO[(4 * g4 + e) * LD + vcol];
 #pragma unroll
-        for (int t = 0; t < NT && CHAIN; ++t) {
-            const f32x4 u = PR::lds_tile(zero4(), sQT + 16 * t * G::LDT, G::LDT, dor, lane);
-            const f32x4 y = PR::lds_tile(zero4(), sKT + 16 * t * G::LDT, G::LDT, dxr, lane);
-            const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * t + 4 * g4);
+        for (int t = 0; t < NTW && CHAIN; ++t) {
+            const int tg = kh * NTW + t;
+            const f32x4 u = PR::lds_tile(zero4(), sQT + 16 * tg * G::LDT, G::LDT, dor, lane);
+            const f32x4 y = PR::lds_tile(zero4(), sKT + 16 * tg * G::LDT, G::LDT, dxr, lane);
+            const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * tg + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
             sched_fence();
@@ -856,9 +887,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     }
     if (CHAIN && d_initial) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4 *>(d_initial + sbase + (int64_t)vcol * D + 16 * t + 4 * g4) =
-                dSs[t];
+        for (int t = 0; t < NTW; ++t)
+            *reinterpret_cast<f32x4 *>(d_initial + sbase + (int64_t)vcol * D +
+                                       16 * (kh * NTW + t) + 4 * g4) = dSs[t];
     }
 }
 
@@ -889,8 +920,14 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
         beta, initial_state, cu_seqlens, static_cast<const T *>(d_out), d_final,              \
         static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv), dlog_alpha, dbeta,   \
         d_initial, ckpt, dckpt, num_seqs, seq_len, total_tokens, H, ready
-    hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChain>), dim3((unsigned)units),
-                       dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+    // the chain: two workgroups per (sequence, head), one per value half, when
+    // the states are ready (the pass that computes them runs on whole heads)
+    if (ready)
+        hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChainHalf>), dim3((unsigned)(2 * units)),
+                           dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+    else
+        hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChain>), dim3((unsigned)units),
+                           dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
     if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdGrad>), dim3((unsigned)(slots * H)),
                        dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
