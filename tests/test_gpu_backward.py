@@ -123,6 +123,24 @@ def test_bwd_packed_ragged():
     assert torch.equal(g["d_initial_state"][5].cpu(), d_fin[5])
 
 
+
+def test_bwd_many_packed_sequences():
+    """70 packed sequences (more than the 64 whose chains are ordered longest
+    first, so the chain runs in sequence order), ragged lengths with empty ones,
+    three heads: every gradient of every sequence against the oracle."""
+    rng = np.random.default_rng(640)
+    lens = [int(x) for x in rng.integers(0, 48, size=70)]
+    lens[3] = lens[40] = 0
+    w = synth.WORKLOADS["varlen_16"]
+    inp = packed_parts(lens, lambda i, n: synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=3,
+                                                               seed=900 + i))
+    d_out, d_fin = loss_grads(inp, 13)
+    say("bwd 70 packed", sum(lens))
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label="bwd 70 packed")
+    assert torch.equal(g["d_initial_state"][3].cpu(), d_fin[3])
+    assert torch.equal(g["d_initial_state"][40].cpu(), d_fin[40])
+
 def test_bwd_without_states():
     """No initial state, no final-state gradient, no initial-state gradient."""
     inp = synth.prefill_inputs("prefill_4k", seq_len=300, heads=2)
