@@ -37,9 +37,11 @@
 //   1. every chunk's entering state S0 into the workspace (the prefill kernel's
 //      states mode; for fp32 at d = 128 the chain kernel's pass 1 instead);
 //   2. the chain kernel, two workgroups per (sequence, head), one per half of
-//      the value columns (kBwdChainHalf; kBwdChain, one workgroup per head,
-//      where pass 1 runs in it): the dS recursion over the chunks in reverse,
-//      dS_C of every chunk into the workspace's second region;
+//      the value columns (kBwdChainHalf; four, kBwdChainQuarter, at d = 128
+//      when four per pair still fit on the device's CUs; kBwdChain, one
+//      workgroup per head, where pass 1 runs in it): the dS recursion over the
+//      chunks in reverse, dS_C of every chunk into the workspace's second
+//      region;
 //   3. the gradient kernel (kBwdGrad), one workgroup per (16-token slot, head):
 //      every other gradient of its chunk from its S0 and dS_C.
 // D / 16 waves per workgroup.  States are held in registers in two
@@ -47,6 +49,8 @@
 // contract over d_k) and key columns 16w.. of M = S^T (for products that
 // contract over d_v), so no product needs a cross-wave reduction.  Chunk
 // operands are staged in LDS as fp32.
+#include <atomic>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -414,10 +418,11 @@ template <> struct RawIn<float> {
 // owning half of the value columns (the columns of dL/dS evolve independently):
 // its wave w holds 16 value columns for half of the key tiles, so the one
 // product that contracts over d_k (K_end dS) sums two waves' halves in LDS;
+// kBwdChainQuarter likewise with four workgroups and quarters;
 // kBwdGrad runs one workgroup per (16-token slot, head) and forms every
 // other gradient of its chunk from the chunk's entering state (`ckpt`) and
 // end gradient (`dckpt`), independently of all other chunks.
-constexpr int kBwdChain = 1, kBwdGrad = 2, kBwdChainHalf = 3;
+constexpr int kBwdChain = 1, kBwdGrad = 2, kBwdChainHalf = 3, kBwdChainQuarter = 4;
 
 template <typename T, int D, int BMODE>
 __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
@@ -440,14 +445,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
     float *sSD = sm + G::oSD, *sAt = sm + G::oAt;
     float *sQT = sm + G::oQT, *sKT = sm + G::oKT;  // chain kernel only
-    constexpr bool HALF = BMODE == kBwdChainHalf;
-    // the half-column chain: key tiles per wave, and this wave's half of them
-    constexpr int NTW = HALF ? NT / 2 : NT;
+    // the split chain: workgroups per (sequence, head) and key tiles per wave
+    constexpr int PARTS = BMODE == kBwdChainHalf ? 2 : BMODE == kBwdChainQuarter ? 4 : 1;
+    constexpr int NTW = NT / PARTS, VG = G::W / PARTS;  // VG: value groups per workgroup
+    static_assert(PARTS == 1 || sizeof(T) == 4 || NTW % 2 == 0, "bf16 products take tile pairs");
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.x % H;
-    const int kh = HALF ? w / (G::W / 2) : 0;
-    const int vhalf = HALF ? (int)((blockIdx.x / H) & 1) : 0;
+    const int kh = w / VG;  // the split chain: this wave's part of the key tiles
+    const int vpart = (int)((blockIdx.x / H) % PARTS);  // and its workgroup's value part
     // first token of sequence m (offsets clamped into [0, total_tokens])
     auto seq_begin = [&](int m) -> int64_t {
         if (!cu_seqlens) return (int64_t)m * seq_len;
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         n = lo;
         cfix = (int)(slot - (seq_begin(n) / kBC + n));
     } else {
-        n = HALF ? (int)(blockIdx.x / H >> 1) : (int)(blockIdx.x / H);
+        n = (int)(blockIdx.x / H / PARTS);
         if (cu_seqlens && num_seqs <= 64) {
             // packed: the chains of the longest sequences go first (workgroups
             // are dispatched in index order); lane m ranks sequence m by its
@@ -515,9 +521,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                      : dckpt + ((tbeg / kBC + n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
-    // S orientation: this lane's value column (the half-column chain: wave
-    // w % (W / 2) of value half vhalf)
-    const int vcol = HALF ? D / 2 * vhalf + 16 * (w % (G::W / 2)) + r : 16 * w + r;
+    // S orientation: this lane's value column (the split chain: value group
+    // w % VG of value part vpart)
+    const int vcol = D / PARTS * vpart + 16 * (w % VG) + r;
     const int kcol = 16 * w + r;  // M orientation: this lane's key column
 
     // Stage chunk c: raw rows as fp32, the prefix G, K+, K-, Q+, Ke, gam, the
@@ -750,15 +756,21 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + (vcol - r), LD, lane);
         const f32x4 dde = PR::lds_reg(zero4(), sKe + 16 * NTW * kh, LD, dSs, lane);
         f32x4 ddl;
-        if constexpr (HALF) {
-            // the other key half's partial from the partner wave (same value
-            // columns), summed in one order in both waves
+        if constexpr (PARTS > 1) {
+            // the partials of the waves with the same value columns (one per
+            // part of the key tiles), summed in one order in all of them
             f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
             sx[w * 64 + lane] = dde;
             __syncthreads();
-            const f32x4 o = sx[(w ^ (G::W / 2)) * 64 + lane];
+            f32x4 o = sx[(w % VG) * 64 + lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + (kh == 0 ? dde[e] + o[e] : o[e] + dde[e]);
+            for (int j = 1; j < PARTS; ++j) {
+                const f32x4 p = sx[(w % VG + VG * j) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] += p[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + o[e];
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) ddl[e] = ddm[e] + dde[e];
@@ -893,6 +905,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     }
 }
 
+// Compute units of the current device (0 if the query fails), cached per device.
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64 && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <typename T, int D>
 int launch_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
                const float *beta, const float *initial_state, const int32_t *cu_seqlens,
@@ -921,8 +945,13 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
         static_cast<T *>(dq), static_cast<T *>(dk), static_cast<T *>(dv), dlog_alpha, dbeta,   \
         d_initial, ckpt, dckpt, num_seqs, seq_len, total_tokens, H, ready
     // the chain: two workgroups per (sequence, head), one per value half, when
-    // the states are ready (the pass that computes them runs on whole heads)
-    if (ready)
+    // the states are ready (the pass that computes them runs on whole heads);
+    // four at d = 128 when four per pair still fit on the device's CUs
+    if (D == 128 && ready && 4 * units <= device_cus())
+        hipLaunchKernelGGL((chunk_bwd_kernel<T, D, D == 128 ? kBwdChainQuarter : kBwdChainHalf>),
+                           dim3((unsigned)(4 * units)), dim3(BwdCfg<D>::THREADS), 0, stream,
+                           KDA_BWD_KERNEL_ARGS);
+    else if (ready)
         hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChainHalf>), dim3((unsigned)(2 * units)),
                            dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
     else
