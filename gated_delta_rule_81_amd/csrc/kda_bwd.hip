@@ -548,7 +548,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         R.b = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
         return R;
     };
-    auto prep = [&](int c, bool with_grad, const RawIn<T> &R) -> int {
+    // `late` runs in every wave after its share of the 16 x 16 work, before the
+    // closing barrier (the waves without such work run it while wave 0 solves)
+    auto prep = [&](int c, bool with_grad, const RawIn<T> &R, auto &&late) -> int {
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
         {
@@ -647,6 +649,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                 sM[i * LS + r] = r <= i ? m[e] : 0.f;
             }
         }
+        late();
         __syncthreads();
         return nval;
     };
@@ -661,7 +664,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                                     initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * g4)
                               : zero4();
     for (int c = 0; BMODE == kBwdChain && !states_ready && c < nch; ++c) {
-        prep(c, false, raw_load(c, false, true));
+        prep(c, false, raw_load(c, false, true), [] {});
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             ckpt_store<T>(ck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4, Ss[t]);
@@ -733,7 +736,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             for (int e = 0; e < 4; ++e)
                 Sm[t][e] = ckpt_load1<T>(ck, s0 + (int64_t)(16 * t + 4 * g4 + e) * D + kcol);
         }
-        const int nval = prep(c, true, cur);
+        // the split chain's K_end dS partial (K_end is staged before the 16 x 16
+        // work), published for the partner waves before prep's closing barrier
+        f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
+        f32x4 dde = zero4();
+        const int nval = prep(c, true, cur, [&] {
+            if constexpr (PARTS > 1) {
+                dde = PR::lds_reg(zero4(), sKe + 16 * NTW * kh, LD, dSs, lane);
+                sx[w * 64 + lane] = dde;
+            }
+        });
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
         f32x4 x = zero4(), dl = zero4();
@@ -754,14 +766,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // straight in as the other's accumulator has produced wrong values in
         // two of the four accumulator components when scheduled back to back
         const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + (vcol - r), LD, lane);
-        const f32x4 dde = PR::lds_reg(zero4(), sKe + 16 * NTW * kh, LD, dSs, lane);
+        if constexpr (PARTS == 1) dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
         f32x4 ddl;
         if constexpr (PARTS > 1) {
             // the partials of the waves with the same value columns (one per
-            // part of the key tiles), summed in one order in all of them
-            f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
-            sx[w * 64 + lane] = dde;
-            __syncthreads();
+            // part of the key tiles, written before prep's closing barrier),
+            // summed in one order in all of them
             f32x4 o = sx[(w % VG) * 64 + lane];
 #pragma unroll
             for (int j = 1; j < PARTS; ++j) {
