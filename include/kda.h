@@ -228,8 +228,10 @@ int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_head
  * (1) a forward pass writes every chunk's entering state to the workspace (bf16
  * at d 64 or 128 and fp32 at d 64: the prefill kernel in a states-only mode,
  * 32 tokens per step; fp32 at d 128: 16-token steps at the start of launch 2);
- * (2) one workgroup per (sequence, head) carries dL/dS backwards over the
- * chunks, which needs no forward state, and writes the gradient at every
+ * (2) two workgroups per (sequence, head), one per half of the value columns
+ * (four at d 128 when four per pair fit on the device's compute units; one
+ * where launch 2 also computes the states), carry dL/dS backwards over the
+ * chunks, which needs no forward state, and write the gradient at every
  * chunk's end to the workspace; (3) one workgroup per (chunk, head) forms all
  * other gradients of its chunk from those two states.
  *
