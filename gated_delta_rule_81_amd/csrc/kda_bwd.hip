@@ -702,6 +702,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     RawIn<T> nxt;
     if (CHAIN && nch > 0) nxt = raw_load(nch - 1, true, false);
     for (int c = GRAD ? cfix : nch - 1; c >= (GRAD ? cfix : 0); --c) {
+        if constexpr (CHAIN) {
+            // the chain's dO rows and beta alternate between two buffers by chunk
+            // parity (the second ones in the gradient kernel's dDelta and dbeta
+            // space): they are the only staged arrays read after prep's closing
+            // barrier, so the next chunk's staging cannot overwrite what a slower
+            // wave still reads, and no barrier closes the chunk
+            sDO = (c & 1) ? sm + G::oDl : sm + G::oDO;
+            sBeta = (c & 1) ? sm + G::oDB : sm + G::oBeta;
+        }
         RawIn<T> cur;
         if constexpr (CHAIN) {
             cur = nxt;
@@ -905,7 +914,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             for (int e = 0; e < 4; ++e) dSs[t][e] = gm[e] * dSs[t][e] + u[e] - y[e];
             sched_fence();
         }
-        if constexpr (CHAIN) __syncthreads();
     }
     if (CHAIN && d_initial) {
 #pragma unroll
