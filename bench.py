@@ -16,10 +16,14 @@ Output: one JSON line (rank 0).  ``value`` is prefill tokens/s
 (B*T / mean kda_chunk_fwd time); the decode figure (state-update GB/s) is in
 ``decode``; ``ms_per_step`` is the wall time per step (both kernels).
 ``roofline`` is for kda_chunk_fwd and ``decode.roofline`` for the decode
-kernel, both against HBM (8 TB/s).  ``cpu_baseline`` is the fp64 oracle on
-the host cores over a bounded sample of the prefill workload.
+kernel, both against HBM (8 TB/s).  ``workloads`` times kda_chunk_fwd alone on
+the other prefill configurations (tiny fp32, the 4K layer with the Infinity
+Cache flushed between repetitions, 16 packed sequences).  ``cpu_baseline`` is
+the fp64 oracle on the host cores over all heads of the prefill workload, and
+``parity`` compares the timed run's out and final state with it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--no-workloads]       (leave out the other prefill configurations)
        [--copy-calibration]   (adds 1 GiB device copies after timing, used to
                                scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
        [--skip-decode]        (decode workload shrunk to one session-head; for
@@ -27,7 +31,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--backward [--bwd-workload k3_prefill_32k|prefill_4k|varlen_16]]
                               (instead: kda_chunk_bwd, the gradients of the
                                prefill, on its own JSON line)
-       [--prefill-workload prefill_4k|varlen_16|k3_prefill_32k]
+       [--prefill-workload tiny|prefill_4k|varlen_16|k3_prefill_32k]
                               (instead: kda_chunk_fwd alone on that workload, dense
                                or packed; its own JSON line)
        [--segments G [--seg-workload long_1m|prefill_4k]]
@@ -50,9 +54,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_DENSE_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
 FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix, published
-# d=128, chunk 32: 6 d^2 for [K+; Q+] S and Kend^T Delta, plus 24,576 for the
-# lower-triangular intra-chunk products (A, Mqk, Delta, Mqk Delta)
-PREFILL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
+
+
+def prefill_flop_per_token_head(d=128, C=64):
+    """Algorithmic flops per token-head of the chunked prefill, the hot-path
+    definition: 6 d_k d_v for the state products ([K+; Q+] S and K_end^T Delta)
+    plus C (3 d_k + 2 d_v) + C^2 / 3 for the triangular in-chunk products,
+    with d_k = d_v = d and C = 64 (140,629 at d = 128)."""
+    return 6 * d * d + C * (3 * d + 2 * d) + C * C / 3
+
+
+# the kernel's own count (32-token chunks): 6 d^2 plus 24,576 for its
+# lower-triangular products (A, Mqk, Delta, Mqk Delta) at d = 128
+KERNEL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_b256.traffic.json")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
@@ -106,26 +120,93 @@ def measured_traffic(path=TRAFFIC_FILE, names=("kda_chunk.hip", "kda_device.h"))
     return doc.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, heads, threads):
+def host_cpu():
+    """CPU model name and the cores in this process's affinity mask."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def oracle_threads():
+    """Threads for the oracle: every core in the affinity mask, unless
+    OMP_NUM_THREADS names the process's share of the host (as it does where
+    one host serves several GPUs)."""
+    _, cores = host_cpu()
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return min(cores, int(env))
+    return cores
+
+
+def _slice_row_errors(got, ref):
+    """Max over heads of the relative L2 error of a [T, h, d] slice, and max
+    over token rows of ||x_t - x*_t|| / max(||x*_t||, the slice's RMS row norm)."""
+    import numpy as np
+    e2 = np.sum((got - ref) ** 2, axis=-1)  # [T, h]
+    r2 = np.sum(ref ** 2, axis=-1)
+    E, R = e2.sum(axis=0), r2.sum(axis=0)
+    slice_err = float(np.max(np.sqrt(E / np.maximum(R, 1e-300))))
+    floor = R / max(ref.shape[0], 1)
+    row = float(np.max(np.sqrt(e2 / np.maximum(np.maximum(r2, floor), 1e-300))))
+    return slice_err, row
+
+
+def cpu_baseline(inp, heads, threads, out_gpu=None, fin_gpu=None, group=16):
     """The fp64 oracle on `heads` heads of the prefill workload over its full
-    length, on the host cores; scaled to tokens/s of the whole workload."""
+    length, on the host cores, `group` heads per call; scaled to tokens/s of
+    the whole workload.  With the GPU's out / final state of the same
+    workload (CPU tensors), also their errors against it on those heads: max
+    relative L2 per head slice and per token (state: value) row."""
     import numpy as np
     import oracle
 
     H = inp["q"].shape[2]
-    f = lambda key: inp[key][0, :, :heads].float().numpy().astype(np.float64)
-    q, k, v, g = (f(key) for key in ("q", "k", "v", "log_alpha"))
-    b = inp["beta"][0, :, :heads].numpy().astype(np.float64)
-    s0 = inp["initial_state"][:, :heads].numpy().astype(np.float64)
-    T = q.shape[0]
-    run = oracle.gdn_forward if g.ndim == 2 else oracle.kda_forward  # scalar or channel gates
-    t0 = time.perf_counter()
-    run(q, k, v, g, b, state0=s0, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": T * heads / dt / H, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{heads} of {H} heads x {T} tokens of the prefill workload, "
-                      f"fp64, {dt:.1f} s; value = sample token-heads/s / {H} heads"}
+    T = inp["q"].shape[1]
+    run = oracle.gdn_forward if inp["log_alpha"].dim() == 3 else oracle.kda_forward
+    f = lambda t, h0, h1: t[0, :, h0:h1].float().numpy().astype(np.float64)
+    dt = 0.0
+    errs = [0.0, 0.0, 0.0, 0.0]  # out slice, out row, state slice, state row
+    for h0 in range(0, heads, group):
+        h1 = min(heads, h0 + group)
+        q, k, v, g = (f(inp[key], h0, h1) for key in ("q", "k", "v", "log_alpha"))
+        b = inp["beta"][0, :, h0:h1].numpy().astype(np.float64)
+        s0 = inp["initial_state"][:, h0:h1].numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        ref_out, ref_fin = run(q, k, v, g, b, state0=s0, threads=threads)
+        dt += time.perf_counter() - t0
+        del q, k, v, g, b
+        if out_gpu is not None:
+            e = _slice_row_errors(f(out_gpu, h0, h1), ref_out)
+            errs[0], errs[1] = max(errs[0], e[0]), max(errs[1], e[1])
+            # states: value rows of [h, d_v, d_k] as the token rows of one "slice" per head
+            fs = fin_gpu[0, h0:h1].numpy().astype(np.float64).transpose(1, 0, 2)
+            e = _slice_row_errors(fs, ref_fin[0].transpose(1, 0, 2))
+            errs[2], errs[3] = max(errs[2], e[0]), max(errs[3], e[1])
+    model, cores = host_cpu()
+    res = {"value": T * heads / dt / H, "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{heads} of {H} heads x {T} tokens of the prefill workload, "
+                     f"fp64, {dt:.1f} s in the oracle; value = sample token-heads/s / {H} "
+                     f"heads",
+           "cpu_model": model, "affinity_cores": cores}
+    parity = None
+    if out_gpu is not None:
+        parity = {"heads_checked": heads, "of_heads": H, "tokens": T,
+                  "out_rel_l2_max": errs[0], "out_row_max": errs[1],
+                  "state_rel_l2_max": errs[2], "state_row_max": errs[3],
+                  "tol": 2e-2, "row_tol": 4e-2,
+                  "metric": "relative L2 per (head) slice, max over slices; rows: "
+                            "||x_r - x*_r|| / max(||x*_r||, slice RMS row norm)"}
+        parity["pass"] = (errs[0] <= 2e-2 and errs[2] <= 2e-2 and errs[1] <= 4e-2
+                          and errs[3] <= 4e-2)
+    return res, parity
 
 
 def attainable_peaks(torch):
@@ -180,15 +261,21 @@ def bwd_bytes(T_tokens, H, d, n_seqs, esz=2):
     return T_tokens * H * per_token_head + 3 * n_seqs * H * d * d * 4
 
 
-def bench_prefill_workload(torch, args):
-    """kda_chunk_fwd alone on one named prefill workload (dense or packed;
-    inputs seeded and resident in HBM), timed with HIP events."""
+# Infinity Cache (MALL) size of the MI355X: workloads smaller than this are
+# timed with a write of twice its size between repetitions, outside the timed
+# region, so every repetition reads its inputs from HBM.
+MALL_BYTES = 256 << 20
+
+
+def time_prefill(torch, kda, name, steps, warmup, flush=None):
+    """kda_chunk_fwd on one named prefill workload (dense or packed; inputs
+    seeded and resident in HBM), each repetition timed with HIP events on the
+    launch stream.  flush=None: flush the MALL between repetitions when the
+    workload's bytes fit in it."""
     import synth
-    import gated_delta_rule_81_amd as kda
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.prefill_workload]
+    w = synth.WORKLOADS[name]
     log("generating", w.notes)
     inp = synth.prefill_inputs(w)
     P = {key: inp[key].to(dev) for key in ("q", "k", "v", "log_alpha", "beta")}
@@ -196,48 +283,71 @@ def bench_prefill_workload(torch, args):
     s0 = None if s0 is None else s0.to(dev)
     cu = inp.get("cu_seqlens")
     cu = None if cu is None else cu.to(dev)
+    del inp
     B, T, H, D = P["q"].shape
     n_seqs = (cu.numel() - 1) if cu is not None else B
     out = torch.empty_like(P["v"])
     fin = torch.empty((n_seqs, H, D, D), dtype=torch.float32, device=dev)
+    tokens = B * T
+    esz = P["q"].element_size()
+    nbytes = prefill_bytes(tokens, H, D, n_seqs, esz=esz)
+    if s0 is None:  # no initial state is read
+        nbytes -= n_seqs * H * D * D * 4
+    if flush is None:
+        flush = nbytes < MALL_BYTES
+    scratch = torch.empty(2 * MALL_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
     torch.cuda.synchronize()
 
     def step():
         kda.chunk_fwd(P["q"], P["k"], P["v"], P["log_alpha"], P["beta"], s0, cu, out=out,
                       final_state=fin)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    K = args.steps
     stream = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    log(f"timing {K} x kda_chunk_fwd on {w.name}")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    log(f"timing {steps} x kda_chunk_fwd on {w.name}" + (" (MALL flushed)" if flush else ""))
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for s in range(K):
+    for s in range(steps):
+        if scratch is not None:
+            scratch.fill_(float(s))
+        ev[s][0].record(stream)
         step()
-        ev[s + 1].record(stream)
+        ev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(K)]
-    avg = sum(ms) / K
-    tokens = B * T
-    nbytes = prefill_bytes(tokens, H, D, n_seqs, esz=P["q"].element_size())
-    if s0 is None:  # no initial state is read
-        nbytes -= n_seqs * H * D * D * 4
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    avg = sum(ms) / steps
     gbs = nbytes / (avg * 1e-3) / 1e9
-    log(f"kda_chunk_fwd on {w.name}: avg {avg:.3f} ms (min {min(ms):.3f})")
-    return {"metric": f"KDA chunked-fwd tokens/s ({w.name})", "value": tokens / (avg * 1e-3),
-            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-            "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16" if P["q"].dtype == torch.bfloat16 else "f32",
-            "data": "synthetic",
-            "config": {"workload": f"kda_chunk_fwd {w.name}: {w.notes}", "tokens": tokens,
-                       "sequences": n_seqs, "heads": H, "head_dim": D},
+    log(f"kda_chunk_fwd on {w.name}: avg {avg:.4f} ms (min {ms[0]:.4f})")
+    return {"workload": f"kda_chunk_fwd {w.name}: {w.notes}", "tokens": tokens,
+            "sequences": n_seqs, "heads": H, "head_dim": D,
+            "dtype": "bf16" if esz == 2 else "f32",
+            "tokens_per_s": tokens / (avg * 1e-3), "kernel_ms_avg": avg, "kernel_ms_min": ms[0],
+            "kernel_ms_median": ms[steps // 2], "algorithmic_bytes": nbytes,
+            "mall_flushed": bool(flush), "wall_s": wall,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
-            "kernel_ms_avg": avg, "kernel_ms_min": min(ms), "algorithmic_bytes": nbytes,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+
+
+def bench_prefill_workload(torch, args):
+    """kda_chunk_fwd alone on one named prefill workload, its own JSON line."""
+    import gated_delta_rule_81_amd as kda
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    r = time_prefill(torch, kda, args.prefill_workload, args.steps, args.warmup)
+    return {"metric": f"KDA chunked-fwd tokens/s ({args.prefill_workload})",
+            "value": r["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["wall_s"] / args.steps * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": r["dtype"], "data": "synthetic",
+            "config": {"workload": r["workload"], "tokens": r["tokens"],
+                       "sequences": r["sequences"], "heads": r["heads"],
+                       "head_dim": r["head_dim"], "mall_flushed": r["mall_flushed"]},
+            "roofline": r["roofline"], "kernel_ms_avg": r["kernel_ms_avg"],
+            "kernel_ms_min": r["kernel_ms_min"], "algorithmic_bytes": r["algorithmic_bytes"],
             "cpu_baseline": None}
 
 
@@ -404,6 +514,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="leave out the timings of the other prefill configurations "
+                         "(tiny, prefill_4k, varlen_16) from the default line")
     ap.add_argument("--cpu-heads", type=int, default=96)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
@@ -428,7 +541,7 @@ def main():
                     choices=["k3_prefill_32k", "prefill_4k", "varlen_16"],
                     help="the prefill workload --backward runs on")
     ap.add_argument("--prefill-workload", default=None,
-                    choices=["prefill_4k", "varlen_16", "k3_prefill_32k"],
+                    choices=["tiny", "prefill_4k", "varlen_16", "k3_prefill_32k"],
                     help="time kda_chunk_fwd alone on this workload instead (its own JSON line)")
     args = ap.parse_args()
     if args.scalar_gate and args.snapshot_every:
@@ -544,7 +657,9 @@ def main():
     dbytes = decode_bytes(w_dec.batch, w_dec.heads, w_dec.head_dim, gate_width=gw)
     pre_gbs = pbytes / (pre_avg * 1e-3) / 1e9
     dec_gbs = dbytes / (dec_avg * 1e-3) / 1e9
-    pre_tflops = PREFILL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
+    pre_tflops = (prefill_flop_per_token_head(w_pre.head_dim) * T_tok * w_pre.heads
+                  / (pre_avg * 1e-3) / 1e12)
+    kern_tflops = KERNEL_FLOP_PER_TOKEN_HEAD * T_tok * w_pre.heads / (pre_avg * 1e-3) / 1e12
     traffic = measured_traffic() if every == 0 and not sg else None
     dec_traffic = (measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)
                    if not sg and not args.skip_decode else None)
@@ -579,7 +694,10 @@ def main():
         "prefill": {"kernel_ms_avg": pre_avg, "kernel_ms_min": pre_ms[0],
                     "kernel_ms_median": pre_ms[K // 2], "algorithmic_bytes": pbytes,
                     "mfma_bf16_tflops_algorithmic": pre_tflops,
-                    "mfma_frac_algorithmic": pre_tflops / BF16_DENSE_PEAK_TFLOPS},
+                    "mfma_frac_algorithmic": pre_tflops / BF16_DENSE_PEAK_TFLOPS,
+                    "mfma_flop_per_token_head": prefill_flop_per_token_head(w_pre.head_dim),
+                    "mfma_frac_kernel_count": kern_tflops / BF16_DENSE_PEAK_TFLOPS,
+                    "kernel_flop_per_token_head": KERNEL_FLOP_PER_TOKEN_HEAD},
         "decode": {"metric": "decode state-update HBM GB/s", "value": dec_gbs, "unit": "GB/s",
                    "kernel_ms_avg": dec_avg, "kernel_ms_min": dec_ms[0],
                    "algorithmic_bytes": dbytes, "tokens_per_s": w_dec.batch / (dec_avg * 1e-3),
@@ -587,13 +705,22 @@ def main():
                                 "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
                                 "traffic": dec_traffic}},
     }
+    if not args.no_workloads:
+        # the other prefill configurations, each timed alone after the step loop
+        result["workloads"] = {}
+        for name in ("tiny", "prefill_4k", "varlen_16"):
+            result["workloads"][name] = time_prefill(torch, kda, name, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        threads = len(os.sched_getaffinity(0))
-        threads = max(1, min(threads, 16))
-        log(f"cpu baseline: oracle on {args.cpu_heads} heads, {threads} threads")
-        result["cpu_baseline"] = cpu_baseline(pre, args.cpu_heads, threads)
+        threads = oracle_threads()
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads, {threads} threads; "
+            "parity of the timed run's out and final state against it")
+        res, parity = cpu_baseline(pre, args.cpu_heads, threads, out.cpu(), fin.cpu())
+        result["cpu_baseline"] = res
+        result["parity"] = parity
+        log(f"parity: {parity}")
     else:
         result["cpu_baseline"] = None
+        result["parity"] = None
     print(json.dumps(result), flush=True)
 
 

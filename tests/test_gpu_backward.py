@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import synth
-from parity import TOL, f64, max_rel_l2, say, seq_starts
+from parity import (DBETA_ROW_TOL, ROW_TOL, TOL, f64, max_rel_l2, say, seq_starts,
+                    slice_row_errors, state_errors)
 
 import gated_delta_rule_81_amd as kda
 
@@ -46,12 +47,12 @@ def oracle_grads(inp, d_out, d_fin, heads=None, threads=0):
     q = inp["q"]
     B, T, H, D = q.shape
     heads = list(range(H)) if heads is None else list(heads)
-    flat = lambda x: f64(x.reshape(B * T, *x.shape[2:]))[:, heads]
+    flat = lambda x: f64(x.reshape(B * T, *x.shape[2:])[:, heads])
     s0 = inp.get("initial_state")
     return oracle.kda_backward(
         flat(q), flat(inp["k"]), flat(inp["v"]), flat(inp["log_alpha"]), flat(inp["beta"]),
-        flat(d_out), d_state=None if d_fin is None else f64(d_fin)[:, heads],
-        state0=None if s0 is None else f64(s0)[:, heads], seq_start=seq_starts(inp),
+        flat(d_out), d_state=None if d_fin is None else f64(d_fin[:, heads]),
+        state0=None if s0 is None else f64(s0[:, heads]), seq_start=seq_starts(inp),
         threads=threads)
 
 
@@ -173,16 +174,47 @@ def test_bwd_prefill_4k_sampled_heads():
     compare(inp, g, oracle_grads(inp, d_out, d_fin, heads), heads=heads, label="bwd prefill_4k")
 
 
-def test_bwd_k3_prefill_32k_sampled_heads():
-    """The 32,768-token x 96-head K3 shape: the full launch, two heads over
-    all tokens against the oracle."""
+def compare_full(inp, g, d_out, d_fin, group=16, label=""):
+    """Every (sequence, head) slice and every row of every gradient against the
+    oracle, heads taken ``group`` at a time.  Rows: token rows of dq, dk, dv,
+    dlog_alpha; single elements of dbeta (bound DBETA_ROW_TOL); value rows of
+    d_initial_state."""
+    q = inp["q"]
+    B, T, H, D = q.shape
+    st = seq_starts(inp)
+    tol, rtol = TOL[q.dtype], ROW_TOL[q.dtype]
+    worst = {name: (0.0, 0.0) for name in GRADS + ("d_initial_state",)}
+    cpu = {name: g[name].cpu() for name in GRADS}
+    dsi = None if g["d_initial_state"] is None else g["d_initial_state"].cpu()
+    for h0 in range(0, H, group):
+        heads = list(range(h0, min(H, h0 + group)))
+        ref = oracle_grads(inp, d_out, d_fin, heads)
+        for name in GRADS:
+            got = f64(cpu[name].reshape(B * T, *cpu[name].shape[2:])[:, h0:h0 + len(heads)])
+            r = ref[name]
+            if name == "dbeta":  # one element per row
+                got, r = got[..., None], r[..., None]
+            e = slice_row_errors(got, r, st)
+            worst[name] = tuple(max(a, b) for a, b in zip(worst[name], e))
+        if dsi is not None:
+            e = state_errors(f64(dsi[:, h0:h0 + len(heads)]), ref["dstate0"])
+            worst["d_initial_state"] = tuple(max(a, b) for a, b in zip(worst["d_initial_state"], e))
+    print(f"{label}: " + " ".join(f"{k} {v[0]:.2e} (row {v[1]:.2e})" for k, v in worst.items())
+          + f" (tol {tol}, row tol {rtol}, dbeta element tol {DBETA_ROW_TOL[q.dtype]})",
+          flush=True)
+    for name, (e_slice, e_row) in worst.items():
+        assert e_slice <= tol, (name, e_slice)
+        assert e_row <= (DBETA_ROW_TOL[q.dtype] if name == "dbeta" else rtol), (name, e_row)
+
+
+def test_bwd_k3_prefill_32k_all_heads():
+    """The 32,768-token x 96-head K3 shape: the full launch, all 96 heads over
+    all tokens, every gradient slice and row, against the oracle."""
     inp = synth.prefill_inputs("k3_prefill_32k")
     d_out, d_fin = loss_grads(inp, 12)
     say("bwd k3 32k")
     g = run_gpu(inp, d_out, d_fin)
-    heads = [0, 95]
-    compare(inp, g, oracle_grads(inp, d_out, d_fin, heads, threads=2), heads=heads,
-            label="bwd k3 32k")
+    compare_full(inp, g, d_out, d_fin, label="bwd k3 32k")
 
 
 def packed_parts(lens, make):

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synth
-from parity import TOL, compare_prefill, f64, max_rel_l2, say
+from parity import check_prefill_full, f64, max_rel_l2, say
 
 import gated_delta_rule_81_amd as kda
 
@@ -24,12 +24,9 @@ def run(inp, **kw):
     return out, fin
 
 
-def check(inp, out, fin, seqs=None, heads=None, label=""):
-    e_out, e_st = compare_prefill(inp, out.cpu(), fin.cpu() if fin is not None else None,
-                                  seqs, heads)
-    tol = TOL[inp["q"].dtype]
-    print(f"{label}: out {e_out:.2e} state {e_st:.2e} (tol {tol})")
-    assert e_out <= tol and e_st <= tol, (e_out, e_st)
+def check(inp, out, fin, label=""):
+    """Every (sequence, head) slice and every row against the oracle."""
+    check_prefill_full(inp, out.cpu(), fin.cpu() if fin is not None else None, label=label)
 
 
 # ---------------------------------------------------------------- small, exhaustive
@@ -183,32 +180,34 @@ def test_no_initial_state_equals_zeros_and_no_final_state():
 
 
 # ---------------------------------------------------------------- workloads
+# Every (sequence, head) slice and every token row of the workloads' outputs and
+# final states against the oracle (check_prefill_full: slice rel-L2 and row
+# bounds).
 def test_prefill_4k_workload_full():
-    """B=1 H=32 T=4096 d=128 bf16, zero state: every head checked."""
+    """B=1 H=32 T=4096 d=128 bf16, zero state: every head, every row."""
     inp = synth.prefill_inputs("prefill_4k")
     say("prefill_4k full")
     out, fin = run(inp)
-    check(inp, out, fin, label="prefill_4k")
+    check_prefill_full(inp, out.cpu(), fin.cpu(), label="prefill_4k")
 
 
-def test_k3_prefill_32k_workload_sampled_heads():
-    """B=1 H=96 T=32768 d=128 bf16, state N(0, 0.02): the full launch, with four
-    heads (first, last, two inner) checked over the whole sequence."""
+def test_k3_prefill_32k_workload_all_heads():
+    """B=1 H=96 T=32768 d=128 bf16, state N(0, 0.02): the full launch, all 96
+    heads over all 32,768 tokens, every token row and state row."""
     inp = synth.prefill_inputs("k3_prefill_32k")
     say("k3_prefill_32k full launch")
     out, fin = run(inp)
-    check(inp, out, fin, heads=[0, 37, 64, 95], label="k3_prefill_32k")
+    check_prefill_full(inp, out.cpu(), fin.cpu(), label="k3_prefill_32k")
 
 
-def test_varlen_16_workload_sampled():
-    """16 packed sequences (U[1024, 65536] tokens), H=32: the full launch, with the
-    shortest and the longest sequence checked on two heads each."""
+def test_varlen_16_workload_all_units():
+    """16 packed sequences (U[1024, 65536] tokens), H=32: the full launch, all
+    16 x 32 (sequence, head) units and every row."""
     inp = synth.prefill_inputs("varlen_16")
     lens = np.diff(inp["cu_seqlens"].numpy())
     say("varlen_16 full launch", int(lens.sum()), "tokens")
     out, fin = run(inp)
-    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
-    check(inp, out, fin, seqs=seqs, heads=[0, 31], label="varlen_16")
+    check_prefill_full(inp, out.cpu(), fin.cpu(), group=8, label="varlen_16")
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from parity import TOL, f64, max_rel_l2, say
+from parity import TOL, Worst, f64, max_rel_l2, say, slice_row_errors, state_errors
 
 import gated_delta_rule_81_amd as kda
 
@@ -54,31 +54,41 @@ def test_decode_small_matches_oracle(dtype, d):
     assert e_out <= tol and e_st <= tol
 
 
-def test_decode_full_size_sampled():
-    """B=256 sessions, H=96, d=128, 64 sequential steps (the decode workload),
-    checked on 48 sampled (session, head) pairs over all 64 steps."""
+def test_decode_full_size_all_units():
+    """B=256 sessions, H=96, d=128, 64 sequential steps (the decode workload):
+    all 24,576 (session, head) units over all 64 steps, every output row (one
+    per step) and every state row against the oracle.  The oracle runs each
+    session's 64 tokens as one sequence: a decode step is the recurrence for
+    one token, so 64 of them in a row are the recurrence over 64 tokens."""
     w = synth.WORKLOADS["decode_b256"]
     inp = synth.decode_inputs(w)
     say("decode full", w.notes)
     state = inp["state"].to(DEV)
     dev_in = {key: inp[key].to(DEV) for key in ("q", "k", "v", "log_alpha", "beta")}
-    rng = np.random.default_rng(0)
-    units = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.batch, 48),
-                                              rng.integers(0, w.heads, 48))]
-    units += [(0, 0), (w.batch - 1, w.heads - 1)]
-    outs = []
+    outs = torch.empty((w.steps, w.batch, w.heads, w.head_dim), dtype=torch.bfloat16,
+                       device=DEV)
     for s in range(w.steps):
-        o = kda.decode_step(*(dev_in[key][s] for key in ("q", "k", "v", "log_alpha", "beta")),
-                            state)
-        outs.append(o[[u[0] for u in units], [u[1] for u in units]].float().cpu())
+        kda.decode_step(*(dev_in[key][s] for key in ("q", "k", "v", "log_alpha", "beta")),
+                        state, out=outs[s])
     torch.cuda.synchronize()
-    out = torch.stack(outs, dim=1)  # [U, steps, dv]
-    fin = state[[u[0] for u in units], [u[1] for u in units]].cpu()
-    ref_out, ref_state = _oracle_steps(inp, w.steps, units)
-    e_out = max_rel_l2([(f64(out[i]), ref_out[i]) for i in range(len(units))])
-    e_st = max_rel_l2([(f64(fin[i]), ref_state[i]) for i in range(len(units))])
-    print(f"decode full sampled: out {e_out:.2e} state {e_st:.2e}")
-    assert e_out <= TOL[torch.bfloat16] and e_st <= TOL[torch.bfloat16]
+    out_gpu = outs.transpose(0, 1).cpu()  # [B, steps, H, d]
+    fin_gpu = state.cpu()
+    del dev_in, outs, state
+    B, S = w.batch, w.steps
+    starts = np.arange(B + 1, dtype=np.int64) * S
+    # [steps, B, H, ...] -> one sequence per session, [B * steps, h, ...]
+    seq = lambda t, h0, h1: f64(t.transpose(0, 1)[:, :, h0:h1].reshape(B * S, h1 - h0,
+                                                                        *t.shape[3:]))
+    worst = Worst()
+    for h0 in range(0, w.heads, 24):
+        h1 = min(w.heads, h0 + 24)
+        ref_out, ref_st = oracle.kda_forward(
+            *(seq(inp[key], h0, h1) for key in ("q", "k", "v", "log_alpha", "beta")),
+            state0=f64(inp["state"][:, h0:h1]), seq_start=starts)
+        got = f64(out_gpu[:, :, h0:h1].reshape(B * S, h1 - h0, -1))
+        worst.add_out(slice_row_errors(got, ref_out, starts))
+        worst.add_state(state_errors(f64(fin_gpu[:, h0:h1]), ref_st))
+    worst.check(torch.bfloat16, "decode full, all units")
 
 
 def test_decode_steps_equal_chunked_prefill():
