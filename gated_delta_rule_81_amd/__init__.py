@@ -9,7 +9,9 @@ Python front end of ``libkda.so``; the C ABI is declared in include/kda.h.
 """
 from ._lib import KdaError, lib
 from .ops import (bwd_workspace_size, chunk_bwd, chunk_fwd, chunk_fwd_segmented,
-                  chunk_fwd_snapshots, decode_step, segmented_workspace_size)
+                  chunk_fwd_segmented_noalloc, chunk_fwd_snapshots, decode_step,
+                  segmented_workspace_size)
 
-__all__ = ["chunk_fwd", "chunk_fwd_segmented", "chunk_fwd_snapshots", "chunk_bwd",
-           "decode_step", "segmented_workspace_size", "bwd_workspace_size", "KdaError", "lib"]
+__all__ = ["chunk_fwd", "chunk_fwd_segmented", "chunk_fwd_segmented_noalloc",
+           "chunk_fwd_snapshots", "chunk_bwd", "decode_step", "segmented_workspace_size",
+           "bwd_workspace_size", "KdaError", "lib"]

@@ -13,10 +13,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_OK = 0
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
+KDA_SCRATCH_BYTES = 64 << 20  # include/kda.h: fixed scratch of the no-allocation entry point
 
 STATUS = {
     0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_UNSUPPORTED",
     -4: "KDA_ERR_ALIGN", -5: "KDA_ERR_ALIAS", -6: "KDA_ERR_DEVICE", -7: "KDA_ERR_LAUNCH",
+    -8: "KDA_ERR_SCRATCH",
 }
 
 # Exported symbols and their C signatures, in include/kda.h order.
@@ -33,6 +35,9 @@ SIGNATURES = {
                                  _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp],
                                 ctypes.c_int),
     "kda_chunk_fwd_segmented_workspace_size": ([_i32, _i32, _i32, _i32], _i64),
+    "kda_chunk_fwd_segmented_noalloc": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp,
+                                         _i32, _i32, _i32, _i32, _i32, _i32, _vp],
+                                        ctypes.c_int),
     "kda_chunk_bwd": ([_vp, _vp, _vp, _fp, _fp, _fp, _vp, _vp, _fp, _vp, _vp, _vp, _fp, _fp,
                        _fp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp],
                       ctypes.c_int),

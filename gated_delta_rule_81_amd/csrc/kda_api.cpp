@@ -3,10 +3,12 @@
 //
 // Validation order: NULL pointers, sizes, supported configurations,
 // alignment, aliasing (all pure host checks, no HIP call), then the device
-// architecture (cached per device), then the launch.
+// architecture (cached per device), then the launch.  Nothing here allocates:
+// workspaces are the caller's, or (kda_chunk_fwd_segmented_noalloc) a fixed
+// buffer compiled into the library.
 #include "kda.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -63,6 +65,7 @@ const char *kda_status_string(int status) {
     case KDA_ERR_ALIAS: return "an output overlaps an input";
     case KDA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
     case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_SCRATCH: return "the request needs more than the library's fixed scratch buffer";
     default: return "unknown status";
     }
 }
@@ -267,6 +270,64 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
                        hipMemcpyDeviceToDevice, stream) != hipSuccess)
         rc = -1;
     return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// The fixed scratch of kda_chunk_fwd_segmented_noalloc: one copy per GPU, in
+// the code object's device memory, reserved when the library's code is
+// loaded on that GPU and held until the process ends.  In host code `scratch`
+// names only a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current, and only
+// that address is ever handed to kernels or copies.
+static __device__ __align__(256) unsigned char scratch[KDA_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void *> g_scratch[kMaxDevices];  // per device: the address of `scratch`
+
+// Device address of the current device's scratch, or NULL if it cannot be had.
+void *scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta,
+                                    const float *initial_state, void *out, float *final_state,
+                                    int32_t seq_len, int32_t num_heads, int32_t head_dim_k,
+                                    int32_t head_dim_v, int32_t num_segments, int32_t dtype,
+                                    hipStream_t stream) {
+    if (num_segments < 1) return KDA_ERR_SHAPE;
+    int st = chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, nullptr, out, final_state,
+                            nullptr, 0, 0, 1, seq_len, num_heads, head_dim_k, head_dim_v, 0,
+                            dtype, false, stream, true);
+    if (st != KDA_OK) return st;
+    const SegPlan sp = seg_plan(seq_len, num_segments);
+    if (sp.nseg <= 1 || num_heads == 0)  // the plain prefill: no scratch
+        return kda_chunk_fwd_segmented(q, k, v, log_alpha, beta, initial_state, out,
+                                       final_state, seq_len, num_heads, head_dim_k, head_dim_v,
+                                       num_segments, dtype, nullptr, 0, stream);
+    const int64_t need =
+        kda_chunk_fwd_segmented_workspace_size(seq_len, num_heads, head_dim_k, num_segments);
+    if (need < 0 || need > (int64_t)KDA_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    st = check_device();
+    if (st != KDA_OK) return st;
+    void *ws = scratch_for_current_device();
+    if (!ws) return KDA_ERR_LAUNCH;
+    return kda_chunk_fwd_segmented(q, k, v, log_alpha, beta, initial_state, out, final_state,
+                                   seq_len, num_heads, head_dim_k, head_dim_v, num_segments,
+                                   dtype, ws, (int64_t)KDA_SCRATCH_BYTES, stream);
 }
 
 int64_t kda_chunk_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs, int32_t num_heads,

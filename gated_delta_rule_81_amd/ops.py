@@ -219,6 +219,40 @@ def chunk_fwd_segmented(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, final_state
 
 
+def chunk_fwd_segmented_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                log_alpha: torch.Tensor, beta: torch.Tensor, num_segments: int,
+                                initial_state: Optional[torch.Tensor], out: torch.Tensor,
+                                final_state: Optional[torch.Tensor]) -> None:
+    """``chunk_fwd_segmented`` into caller-given outputs with the library's
+    fixed scratch instead of a workspace (``kda_chunk_fwd_segmented_noalloc``):
+    this call allocates no device memory, neither here nor in the library.
+    Requests needing more than ``KDA_SCRATCH_BYTES`` raise KDA_ERR_SCRATCH.
+    Calls that may overlap in time on one GPU must not be issued (they share
+    its one scratch buffer)."""
+    if q.dim() != 4 or q.shape[0] != 1:
+        raise ValueError("q must be [1, T, H, d_k]")
+    _, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _expect(q, "q", q.dtype, (1, T, H, dk), dev)
+    _expect(k, "k", q.dtype, (1, T, H, dk), dev)
+    _expect(v, "v", q.dtype, (1, T, H, dv), dev)
+    _expect(log_alpha, "log_alpha", torch.float32, (1, T, H, dk), dev)
+    _expect(beta, "beta", torch.float32, (1, T, H), dev)
+    _expect(initial_state, "initial_state", torch.float32, (1, H, dv, dk), dev)
+    if out is None:
+        raise ValueError("out must be given (this call allocates nothing)")
+    _expect(out, "out", q.dtype, (1, T, H, dv), dev)
+    _expect(final_state, "final_state", torch.float32, (1, H, dv, dk), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().kda_chunk_fwd_segmented_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(out), _ptr(final_state), T, H, dk, dv, int(num_segments), _DTYPES[q.dtype], stream)
+    check(rc, "kda_chunk_fwd_segmented_noalloc")
+
+
 def bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int) -> int:
     """Bytes of workspace ``chunk_bwd`` needs (``kda_chunk_bwd_workspace_size``)."""
     n = lib().kda_chunk_bwd_workspace_size(total_tokens, num_seqs, num_heads, head_dim)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -70,7 +70,8 @@ enum kda_status {
     KDA_ERR_ALIGN = -4,       /* a pointer is not aligned as documented above */
     KDA_ERR_ALIAS = -5,       /* an output overlaps an input it must not */
     KDA_ERR_DEVICE = -6,      /* the current device is not a gfx950 GPU */
-    KDA_ERR_LAUNCH = -7       /* the kernel launch failed (hipGetLastError) */
+    KDA_ERR_LAUNCH = -7,      /* the kernel launch failed (hipGetLastError) */
+    KDA_ERR_SCRATCH = -8      /* needs more than KDA_SCRATCH_BYTES of fixed scratch */
 };
 
 /*
@@ -216,6 +217,31 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
  */
 int64_t kda_chunk_fwd_segmented_workspace_size(int32_t seq_len, int32_t num_heads,
                                                int32_t head_dim, int32_t num_segments);
+
+/*
+ * kda_chunk_fwd_segmented_noalloc -- kda_chunk_fwd_segmented for callers that
+ * cannot allocate device memory (code under stream capture, tight serving
+ * loops, hosts that forbid allocation): its workspace is a fixed buffer of
+ * KDA_SCRATCH_BYTES inside the library, one per GPU, reserved when the
+ * library's code is loaded on that GPU and held until the process ends.  The
+ * call allocates nothing and frees nothing.
+ *
+ * Arguments, rules and result are those of kda_chunk_fwd_segmented without
+ * the workspace.  Requests whose workspace
+ * (kda_chunk_fwd_segmented_workspace_size) exceeds KDA_SCRATCH_BYTES return
+ * KDA_ERR_SCRATCH before any device work; with one segment the call is
+ * kda_chunk_fwd and the scratch is not touched.  Every call on one GPU uses
+ * that GPU's one buffer: calls that may overlap in time on the same GPU (other
+ * streams, other host threads) race and give undefined results; serialise them.
+ * Returns KDA_OK or a kda_status error code.
+ */
+#define KDA_SCRATCH_BYTES (64u << 20) /* 64 MiB: e.g. 4 segments x 32 heads at d = 128 */
+int kda_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta,
+                                    const float *initial_state, void *out, float *final_state,
+                                    int32_t seq_len, int32_t num_heads, int32_t head_dim_k,
+                                    int32_t head_dim_v, int32_t num_segments, int32_t dtype,
+                                    hipStream_t stream);
 
 /*
  * kda_chunk_bwd -- gradients of kda_chunk_fwd: given dL/d out and dL/d

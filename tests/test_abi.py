@@ -15,7 +15,7 @@ from gated_delta_rule_81_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, DEVICE = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, DEVICE, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -8
 BF16, F32 = 1, 0
 
 
@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["kda_abi_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
          "kda_chunk_fwd", "kda_chunk_fwd_scalar_gate",
-         "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_size",
+         "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_noalloc",
+         "kda_chunk_fwd_segmented_workspace_size",
          "kda_chunk_fwd_snapshots", "kda_decode_step", "kda_decode_step_scalar_gate",
          "kda_status_string"])
 
@@ -43,8 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 5
-    for code in range(-7, 1):
+    assert L.kda_abi_version() == 6
+    for code in range(-8, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
 
@@ -294,6 +295,39 @@ def test_segmented_one_segment_needs_no_workspace():
     assert call_seg(seq_len=0, workspace=None, workspace_bytes=0, q=None, k=None, v=None,
                     log_alpha=None, beta=None, out=None) in (DEVICE, OK)
     assert call_seg(num_heads=0, workspace=None, workspace_bytes=0) == OK
+
+
+def call_seg_noalloc(num_segments=4, **kw):
+    kw.setdefault("batch", 1)
+    kw.setdefault("seq_len", 1000)
+    a = chunk_args(**kw)
+    return _lib.lib().kda_chunk_fwd_segmented_noalloc(
+        a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], a["initial_state"], a["out"],
+        a["final_state"], a["seq_len"], a["num_heads"], a["head_dim_k"], a["head_dim_v"],
+        num_segments, a["dtype"], a["stream"])
+
+
+def test_segmented_noalloc_checks():
+    """The fixed-scratch entry point: kda_chunk_fwd_segmented's checks, then the
+    scratch limit, all before any device call."""
+    assert _lib.KDA_SCRATCH_BYTES == 64 << 20
+    assert call_seg_noalloc() in (DEVICE, OK)
+    assert call_seg_noalloc(num_segments=0) == SHAPE
+    assert call_seg_noalloc(q=None) == NULL
+    assert call_seg_noalloc(head_dim_k=96, head_dim_v=96) == UNSUP
+    a = chunk_args()
+    assert call_seg_noalloc(out=a["q"]) == ALIAS
+    # 1M tokens x 32 heads at d = 128: 4 segments need 32 MiB (fits), 16 need
+    # 128 MiB (does not)
+    big = dict(seq_len=1 << 20, num_heads=32)
+    assert seg_size(1 << 20, 32, 128, 4) <= _lib.KDA_SCRATCH_BYTES
+    assert call_seg_noalloc(4, **big) in (DEVICE, OK)
+    assert seg_size(1 << 20, 32, 128, 16) > _lib.KDA_SCRATCH_BYTES
+    assert call_seg_noalloc(16, **big) == SCRATCH
+    # one segment is the plain prefill: no scratch, whatever the size
+    assert call_seg_noalloc(1, seq_len=1 << 20, num_heads=96) in (DEVICE, OK)
+    assert call_seg_noalloc(4, seq_len=1 << 20, num_heads=96) == SCRATCH
+    assert call_seg_noalloc(num_heads=0) == OK
 
 
 # ---------------------------------------------------------------- chunk_bwd
