@@ -251,6 +251,19 @@ def attainable_peaks(torch):
             "gemm": "torch.matmul bf16 8192 x 8192 x 8192"}
 
 
+def copy_calibration(torch):
+    """Three 1 GiB device-to-device copies after the timed work: their
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings give each counter's scale."""
+    dev = torch.device("cuda:0")
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 1 GiB device-to-device copies")
+
+
 def bwd_bytes(T_tokens, H, d, n_seqs, esz=2):
     """Algorithmic HBM bytes of one kda_chunk_bwd: read q, k, v, d_out (esz),
     log_alpha (fp32), beta, the initial state and the final-state gradient;
@@ -560,7 +573,10 @@ def main():
         print(json.dumps(bench_segmented(torch, args)), flush=True)
         return
     if args.backward:
-        print(json.dumps(bench_backward(torch, args)), flush=True)
+        res = bench_backward(torch, args)
+        if args.copy_calibration:
+            copy_calibration(torch)
+        print(json.dumps(res), flush=True)
         return
     if args.prefill_workload:
         print(json.dumps(bench_prefill_workload(torch, args)), flush=True)
@@ -642,13 +658,7 @@ def main():
         f"decode_step avg {dec_avg:.4f} ms (min {dec_ms[0]:.4f})")
 
     if args.copy_calibration:
-        n = 1 << 28  # 1 GiB of fp32
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device-to-device copies")
+        copy_calibration(torch)
 
     T_tok = w_pre.batch * w_pre.seq_len
     gw = 1 if sg else None
