@@ -12,7 +12,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include <atomic>
+#include <vector>
 
 #include "kda_internal.h"
 
@@ -47,6 +51,56 @@ int check_device() {
         g_device_ok[dev].store(st, std::memory_order_relaxed);
     }
     return st == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+// Debug mode (environment variable KDA_DEBUG set to a value other than "0",
+// read at every call): packed-sequence offsets are copied to the host and
+// checked before the launch, and every call waits for its stream and reports
+// any failure of its kernels as KDA_ERR_LAUNCH, with a line on stderr naming
+// the entry point.  Off by default: calls stay asynchronous.
+bool debug_mode() {
+    const char *e = getenv("KDA_DEBUG");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+// Debug mode: cu_seqlens must hold num_seqs + 1 offsets starting at 0,
+// non-decreasing and ending at total.  Returns KDA_OK or KDA_ERR_SHAPE.
+int debug_check_offsets(const int32_t *cu_seqlens, int64_t num_seqs, int64_t total,
+                        hipStream_t stream, const char *where) {
+    if (!cu_seqlens) return KDA_OK;
+    std::vector<int32_t> cu((size_t)num_seqs + 1);
+    if (hipStreamSynchronize(stream) != hipSuccess ||
+        hipMemcpy(cu.data(), cu_seqlens, cu.size() * 4, hipMemcpyDeviceToHost) != hipSuccess) {
+        fprintf(stderr, "[kda debug] %s: cannot read cu_seqlens\n", where);
+        return KDA_ERR_LAUNCH;
+    }
+    bool ok = cu[0] == 0 && cu[(size_t)num_seqs] == total;
+    for (size_t i = 0; ok && i < (size_t)num_seqs; ++i) ok = cu[i] <= cu[i + 1];
+    if (!ok) {
+        fprintf(stderr, "[kda debug] %s: cu_seqlens is not 0 = c0 <= c1 <= ... <= cN = %lld\n",
+                where, (long long)total);
+        return KDA_ERR_SHAPE;
+    }
+    return KDA_OK;
+}
+
+// The status of a call whose launches returned `rc` (0 = queued): in debug
+// mode also wait for the stream and check what its kernels did.
+int launch_status(int rc, hipStream_t stream, const char *where) {
+    if (rc != 0) {
+        if (debug_mode()) fprintf(stderr, "[kda debug] %s: launch failed\n", where);
+        return KDA_ERR_LAUNCH;
+    }
+    if (debug_mode()) {
+        const hipError_t e = hipStreamSynchronize(stream);
+        const hipError_t l = hipGetLastError();
+        if (e != hipSuccess || l != hipSuccess) {
+            fprintf(stderr, "[kda debug] %s: %s\n", where,
+                    hipGetErrorString(e != hipSuccess ? e : l));
+            return KDA_ERR_LAUNCH;
+        }
+    }
+    return KDA_OK;
 }
 
 }  // namespace
@@ -137,14 +191,18 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
     }
     if (check_only) return KDA_OK;
     if (nseq == 0 || num_heads == 0) return KDA_OK;
-    const int st = check_device();
+    int st = check_device();
     if (st != KDA_OK) return st;
+    const char *where = snap ? "kda_chunk_fwd_snapshots"
+                             : (scalar_gate ? "kda_chunk_fwd_scalar_gate" : "kda_chunk_fwd");
+    if (debug_mode() && (st = debug_check_offsets(cu_seqlens, nseq, tokens, stream, where)) != KDA_OK)
+        return st;
     const int rc = kda::launch_chunk_fwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
                                          final_state, num_snapshots > 0 ? snapshots : nullptr,
                                          snapshot_every, num_snapshots, (int32_t)nseq, seq_len,
                                          (int32_t)tokens, num_heads, d, dtype, scalar_gate ? 1 : 0,
                                          0, stream);
-    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+    return launch_status(rc, stream, where);
 }
 
 // Shared by kda_decode_step and kda_decode_step_scalar_gate (log_alpha [B, H]).
@@ -178,7 +236,8 @@ int decode_impl(const void *q, const void *k, const void *v, const float *log_al
     if (st != KDA_OK) return st;
     const int rc = kda::launch_decode_step(q, k, v, log_alpha, beta, state, out, (int64_t)units,
                                            d, dtype, scalar_gate ? 1 : 0, stream);
-    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+    return launch_status(rc, stream,
+                         scalar_gate ? "kda_decode_step_scalar_gate" : "kda_decode_step");
 }
 
 // Segment plan of the segmented prefill: segments of seg_len tokens (a
@@ -269,7 +328,7 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
         hipMemcpyAsync(final_state, Fin + (uint64_t)(n - 1) * num_heads * d * d, hs,
                        hipMemcpyDeviceToDevice, stream) != hipSuccess)
         rc = -1;
-    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+    return launch_status(rc, stream, "kda_chunk_fwd_segmented");
 }
 
 }  // extern "C"
@@ -387,14 +446,17 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
             if (overlap(outputs[i], outputs[j])) return KDA_ERR_ALIAS;
     }
     if (!work) return KDA_OK;
-    const int st = check_device();
+    int st = check_device();
     if (st != KDA_OK) return st;
+    if (debug_mode() &&
+        (st = debug_check_offsets(cu_seqlens, nseq, tokens, stream, "kda_chunk_bwd")) != KDA_OK)
+        return st;
     const int rc = kda::launch_chunk_bwd(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
                                          d_out, d_final_state, dq, dk, dv, dlog_alpha, dbeta,
                                          d_initial_state, static_cast<float *>(workspace),
                                          (int32_t)nseq, seq_len, (int32_t)tokens, num_heads, d,
                                          dtype, stream);
-    return rc == 0 ? KDA_OK : KDA_ERR_LAUNCH;
+    return launch_status(rc, stream, "kda_chunk_bwd");
 }
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -35,6 +35,12 @@
  *     validated on the host before any HIP call, so errors are reported
  *     without touching the device.  Calls on different streams may run
  *     concurrently if their outputs do not overlap.
+ *   - Debug mode: with the environment variable KDA_DEBUG set (to anything
+ *     but "0"; read at every call) each call also copies packed-sequence
+ *     offsets to the host and rejects malformed ones (KDA_ERR_SHAPE) before
+ *     launching, then waits for its stream and reports a failure of its
+ *     kernels as KDA_ERR_LAUNCH, with a line on stderr naming the entry point.
+ *     Calls are then synchronous; results are unchanged.
  *   - Supported now: d_k == d_v in {64, 128}, and for kda_chunk_fwd
  *     num_heads * d_k <= 8388607 (64 tokens of one tensor must span less
  *     than 2^31 bytes).  Other valid sizes return KDA_ERR_UNSUPPORTED.

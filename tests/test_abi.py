@@ -490,3 +490,14 @@ def test_decode_scalar_gate_checks():
     # [B, H] = 4 * 3 floats = 48 bytes
     assert call_decode_sg(out=a["log_alpha"] + 48) in (DEVICE, OK)
     assert call_decode_sg(out=a["log_alpha"] + 32) == ALIAS
+
+
+def test_debug_mode_keeps_host_validation(monkeypatch):
+    """KDA_DEBUG adds device-side checks after validation; the host checks
+    and their codes are unchanged, and without a GPU a valid call still stops
+    at the device check."""
+    monkeypatch.setenv("KDA_DEBUG", "1")
+    assert call_chunk(q=None) == NULL
+    assert call_chunk(head_dim_k=96, head_dim_v=96) == UNSUP
+    assert call_chunk() in (DEVICE, OK)
+    assert call_seg(workspace=None) == NULL
