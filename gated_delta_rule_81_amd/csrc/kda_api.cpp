@@ -39,6 +39,20 @@ bool overlap(const Range &a, const Range &b) {
     return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+std::atomic<int> g_device_cus[kMaxDevices];
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 int check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KDA_ERR_DEVICE;
@@ -302,6 +316,14 @@ int kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const f
         if (overlap(rw, r)) return KDA_ERR_ALIAS;
     st = check_device();
     if (st != KDA_OK) return st;
+    // The segmented call does about three times the chunk work in exchange for
+    // parallelism along the sequence, so it can only win while the plain
+    // launch leaves at least two thirds of the compute units idle.
+    const int cus = device_cus();
+    if (cus > 0 && 3 * (int64_t)num_heads * kda::chunk_fwd_slices(d, dtype) > cus)
+        return chunk_fwd_impl(q, k, v, log_alpha, beta, initial_state, nullptr, out,
+                              final_state, nullptr, 0, 0, 1, seq_len, num_heads, head_dim_k,
+                              head_dim_v, 0, dtype, false, stream);
     unsigned char *ws = static_cast<unsigned char *>(workspace);
     int32_t *cu = reinterpret_cast<int32_t *>(ws);
     float *Y = reinterpret_cast<float *>(ws + cu_b);

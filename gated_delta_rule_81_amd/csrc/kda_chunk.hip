@@ -1042,6 +1042,11 @@ int launch_dtype(const void *q, const void *k, const void *v, const float *log_a
 
 }  // namespace
 
+int chunk_fwd_slices(int head_dim, int dtype) {
+    if (dtype == kDtypeBf16) return head_dim / 64;
+    return head_dim / 16;
+}
+
 int launch_chunk_states(const void *q, const void *k, const void *v, const float *log_alpha,
                         const float *beta, const float *initial_state,
                         const int32_t *cu_seqlens, float *states, int32_t num_seqs,

@@ -47,6 +47,9 @@ int launch_chunk_states(const void *q, const void *k, const void *v, const float
                         int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
                         int dtype, hipStream_t stream);
 
+// Workgroups the prefill kernel runs per (sequence, head): one per d_v slice.
+int chunk_fwd_slices(int head_dim, int dtype);
+
 // Tokens per chunk of the prefill; snapshot intervals are multiples of it.
 constexpr int kChunkTokens = 32;
 

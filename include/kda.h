@@ -195,7 +195,13 @@ int kda_chunk_fwd_scalar_gate(const void *q, const void *k, const void *v,
  *                    hold L = 32 * ceil(ceil(seq_len / num_segments) / 32)
  *                    tokens (the last one the rest), so ceil(seq_len / L) of
  *                    them run; when that is 1 the call is kda_chunk_fwd and
- *                    the workspace is not touched.
+ *                    the workspace is not touched.  It is kda_chunk_fwd too
+ *                    (workspace untouched; its size is still checked) when the
+ *                    plain prefill's own workgroups, one per head and d_v
+ *                    slice (d_k / 64 slices for bf16, d_k / 16 for fp32),
+ *                    already fill a third of the device's compute units: the
+ *                    segmented call does about three times the work and
+ *                    cannot win there.
  *   workspace        caller-owned device scratch, 256-byte aligned (else
  *                    KDA_ERR_ALIGN), of at least
  *                    kda_chunk_fwd_segmented_workspace_size(seq_len,

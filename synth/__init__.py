@@ -44,6 +44,7 @@ class Workload:
     n_seqs: int = 0       # varlen: number of packed sequences
     len_range: tuple = (0, 0)  # varlen: inclusive length range
     steps: int = 0        # decode: sequential single-token steps
+    draw_block: int = 0   # device draws: tokens per block (0 = the whole sequence at once)
     chunk: int = 64
     notes: str = field(default="", compare=False)
 
@@ -61,6 +62,9 @@ WORKLOADS = {
                           notes="16 packed sequences, lengths U[1024,65536], H=32"),
     "long_1m": Workload("long_1m", heads=32, head_dim=128, dtype="bf16", seed=5,
                         seq_len=1 << 20, notes="B=1 H=32 T=1,048,576 d=128 bf16, zero state"),
+    "long_1m_h96": Workload("long_1m_h96", heads=96, head_dim=128, dtype="bf16", seed=6,
+                            seq_len=1 << 20, draw_block=1 << 16,
+                            notes="B=1 H=96 T=1,048,576 d=128 bf16, zero state"),
     "decode_b256": Workload("decode_b256", heads=96, head_dim=128, dtype="bf16", seed=4,
                             batch=256, steps=64, init_std=0.02,
                             notes="B=256 sessions H=96 d=128, 64 single-token steps"),
@@ -150,8 +154,33 @@ def prefill_inputs(w, device=None, **overrides):
         out["workload"] = w
         return out
     gen = torch.Generator(device=device or "cpu").manual_seed(w.seed)
+    if device is not None and w.draw_block and w.draw_block < w.seq_len:
+        return _blocked_device_draw(w, gen, dt)
     q, k, v, beta, g, s = _draw(gen, (w.batch, w.seq_len), w.heads, w.head_dim, dt,
                                 w.init_std, w.batch)
+    return dict(q=q, k=k, v=v, beta=beta, log_alpha=g, initial_state=s,
+                cu_seqlens=None, workload=w)
+
+
+def _blocked_device_draw(w: Workload, gen, dt):
+    """A device draw one block of ``w.draw_block`` tokens at a time (every
+    tensor of block 0, then of block 1, ...), so that the fp32 temporaries of a
+    very long sequence stay one block in size; the initial state comes last."""
+    dev = gen.device
+    shape = (w.batch, w.seq_len, w.heads, w.head_dim)
+    q = torch.empty(shape, dtype=dt, device=dev)
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    g = torch.empty(shape, dtype=torch.float32, device=dev)
+    beta = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    for t0 in range(0, w.seq_len, w.draw_block):
+        t1 = min(w.seq_len, t0 + w.draw_block)
+        bq, bk, bv, bb, bg, _ = _draw(gen, (w.batch, t1 - t0), w.heads, w.head_dim, dt, 0.0, 0)
+        q[:, t0:t1], k[:, t0:t1], v[:, t0:t1] = bq, bk, bv
+        beta[:, t0:t1], g[:, t0:t1] = bb, bg
+    s = None
+    if w.init_std > 0:
+        s = torch.randn(w.batch, w.heads, w.head_dim, w.head_dim, generator=gen,
+                        device=dev) * w.init_std
     return dict(q=q, k=k, v=v, beta=beta, log_alpha=g, initial_state=s,
                 cu_seqlens=None, workload=w)
 

@@ -24,6 +24,7 @@ int launch_chunk_fwd(const void *, const void *, const void *, const float *, co
                      int32_t, int32_t, int32_t, int32_t, int, int, int, int, hipStream_t) {
     reached("launch_chunk_fwd");
 }
+int chunk_fwd_slices(int, int) { reached("chunk_fwd_slices"); }
 int launch_segment_bounds(int32_t *, int, int, int, hipStream_t) {
     reached("launch_segment_bounds");
 }
