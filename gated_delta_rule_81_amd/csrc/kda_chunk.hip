@@ -32,8 +32,12 @@
 //   * K+, Q+ (chunk-relative, <= |k|, |q|) feed [K+; Q+] S and the block
 //     (1,0) tiles; K- of block 0 (chunk-relative) feeds tiles (0,0), (1,0);
 //   * the diagonal tile (1,1) uses K+, Q+, K- of block 1 relative to rho.
-// Every factor is then bounded by e^{decay over 16 tokens}, so the numerics
-// contract (16-token decay sum > -80 per channel) keeps all of them finite.
+// Every factor is then bounded by e^{decay over 16 tokens}.  Gates may be
+// anything in [0, 1]: a (sequence, head, slice) unit in which some 16-token
+// block decays beyond 2^-100 in some channel (or has alpha = 0) is marked by
+// this fast kernel and recomputed by a second launch of the same kernel
+// (FAR), which takes exactly those chunks token by token in fp32 on the scan
+// side; see chunk_fwd_kernel.
 // K_end = K (.) e^{Gamma_last - Gamma} is applied as (K e^{rho - Gamma}),
 // stored in LDS, times the per-channel f = e^{Gamma_last - rho} in fp32 on the
 // scan side: both factors stay in fp32 range.
@@ -66,6 +70,12 @@ namespace {
 
 constexpr int kC = kChunkTokens;  // chunk length
 constexpr int kBS = 16;  // block / tile size
+// The factorised products of a chunk hold e^{+-(decay within a 16-token
+// block)} in fp32 / bf16 operands.  A chunk in which some channel decays by
+// more than 2^-kFarLog2 over one block (or whose gates are -inf or NaN) is
+// taken token by token on the scan side instead (the exact recurrence in
+// fp32).
+constexpr float kFarLog2 = 100.f;
 
 // Physical position of contraction index i (a key channel or a token) in
 // the LDS operand tiles.  For bf16 the 16x16x32 MFMA reads, in lane group
@@ -119,6 +129,16 @@ struct Cfg {
     static constexpr int sKP = 0, sQP = B_TK, sKET = 2 * B_TK, sMQ = sKET + D * LDT * SZ,
                          sT3 = sMQ + B_TT, sV = sT3 + 3 * B_T16, sGam = sV + kC * LDV * SZ,
                          sF1 = sGam + D * 4, sBeta = sF1 + D * 4, SET = sBeta + kC * 4;
+    // Out-of-range words, one per (preparation wave, lane group): word j sits
+    // in the (never read) padding of K+'s row j / 4.
+    __host__ __device__ static constexpr int flag_offset(int j) {
+        return sKP + (j >> 2) * LDK * SZ + D * SZ + 4 * (j & 3);
+    }
+    static_assert(kPad * SZ >= 16 && 4 * PW <= 4 * kC, "flag words in the row padding");
+    // the fast kernel's sticky word (some chunk of the unit was out of range),
+    // in the padding of K+'s first row (the fix-up kernel's words use it)
+    static constexpr int sMark = sKP + D * SZ;
+
     // preparation scratch
     static constexpr int oKD = 2 * SET, oQD = oKD + kBS * LDK * SZ, oKM = oQD + kBS * LDK * SZ,
                          oAt = oKM + B_TK;
@@ -215,6 +235,19 @@ __device__ __forceinline__ void unpack(const Raw<NW> &x, float *f) {
 #pragma unroll
         for (int i = 0; i < N; ++i) f[i] = __uint_as_float(x.w[i]);
     }
+}
+
+// Four consecutive elements of T (8-byte aligned for bf16, 16 for fp32) as floats.
+__device__ __forceinline__ void load4(const bf16 *p, float (&f)[4]) {
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+    f[0] = __uint_as_float(w[0] << 16);
+    f[1] = __uint_as_float(w[0] & 0xffff0000u);
+    f[2] = __uint_as_float(w[1] << 16);
+    f[3] = __uint_as_float(w[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float *p, float (&f)[4]) {
+    const f32x4 w = *reinterpret_cast<const f32x4 *>(p);
+    f[0] = w[0]; f[1] = w[1]; f[2] = w[2]; f[3] = w[3];
 }
 
 // Two floats as one packed word of T pairs (bf16) or two words (fp32).
@@ -413,7 +446,17 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
 constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
 // LPT (compile time, packed input with at most 64 sequences): workgroups take
 // the sequences longest first (see below); otherwise in sequence order.
-template <typename T, int D, int DVS, bool SG, int MODE, bool LPT>
+// FAR (compile time): false = the fast kernel: every chunk through the
+// factorised products; a (sequence, head, slice) unit with a chunk out of
+// their range (a 16-token block decaying beyond 2^-kFarLog2 in some channel,
+// or a -inf / NaN gate) is marked instead of finished: its final state is
+// left unwritten and the first element of its output slice (of its final
+// state when there are no outputs) is set to NaN.  true = the fix-up kernel,
+// launched right after on the same stream: units without the mark return at
+// once; marked units are recomputed from their initial state, out-of-range
+// chunks token by token (exact recurrence in fp32).  The states mode of the
+// backward uses the fast kernel without marks.
+template <typename T, int D, int DVS, bool SG, int MODE, bool LPT, bool FAR>
 __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
@@ -476,6 +519,15 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         tend = tbeg + seq_len;
     }
     const int nchunks = (int)((tend - tbeg + kC - 1) / kC);
+    constexpr bool MARK = !FAR && MODE != kModeStates;  // the fast kernel marks far units
+    if constexpr (FAR) {
+        // the fix-up pass: only units the fast kernel marked (the same
+        // element for every thread, so the whole workgroup returns together)
+        if (nchunks == 0) return;
+        const float mk = out ? to_f32(out[(tbeg * H + h) * (int64_t)D + v0])
+                             : final_state[((int64_t)n * H + h) * D * D + (int64_t)v0 * D];
+        if (!__builtin_isnan(mk)) return;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index as a scalar: the role branches below contain barriers and
@@ -483,6 +535,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, l4 = lane >> 4;
 
+    // The sticky out-of-range words start cleared in both buffer sets.
+    if (tid < 2) *reinterpret_cast<unsigned *>(smem + tid * G::SET + G::sMark) = 0u;
     // The upper-right 16x16 block of Mqk is never written: zero it once in
     // both buffer sets.
     for (int i = tid; i < 2 * kBS * kBS; i += G::THREADS) {
@@ -649,6 +703,18 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     st4(sQD + r * G::LDK + pc, qd);
                 }
                 if (r == kBS - 1) {
+                    // row 15 holds both blocks' total decay: a block that decays
+                    // beyond 2^-kFarLog2 in one of these channels (or a -inf or
+                    // NaN gate) makes the scan take this chunk token by token
+                    bool far = false;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        far = far || !(d0[e] >= -kFarLog2) || !(d1[e] >= -kFarLog2);
+                    if constexpr (FAR)  // this chunk, read by the scan next tick
+                        *reinterpret_cast<unsigned *>(
+                            PS + G::flag_offset(4 * wave + (lane >> 4))) = far ? 1u : 0u;
+                    else if constexpr (MARK)  // sticky: some chunk of this unit
+                        if (far) *reinterpret_cast<unsigned *>(PS + G::sMark) = 1u;
                     // row 31: f = e^{Gamma_last - rho}, gamma = e^{Gamma_last}
                     *reinterpret_cast<f32x4 *>(pF1 + c) = f32x4{ep1[0], ep1[1], ep1[2], ep1[3]};
                     *reinterpret_cast<f32x4 *>(pGam + c) =
@@ -834,6 +900,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                                 : zero4();
     __syncthreads();
 
+    bool far_next = false;  // the chunk scanned in the next tick is out of range
     for (int tick = 0; nchunks > 0 && tick <= nchunks; ++tick) {
         const bool on = tick > 0;  // scans chunk `tick - 1`
         const unsigned char *SS = smem + ((tick & 1) ^ 1) * G::SET;
@@ -849,9 +916,84 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         f32x4 Dl[2];  // Delta row tiles (tokens 0-15, 16-31), kept for phase 2
         const int64_t tok0 = tbeg + (int64_t)(tick - 1) * kC;
         const int nvalid = (int)((tend - tok0) < kC ? (tend - tok0) : kC);
+        // chunks the preparation flagged as beyond the factorised range are
+        // taken token by token (uniform over the workgroup; the flag was read
+        // in the previous tick, right after the preparation wrote it)
+        const bool far = FAR && on && far_next;
 
         // ---------------------------------------------------------- phase 1
-        if (on) {
+        if (on && far) {
+            // The recurrence itself, token by token, in fp32: S' = Diag(a) S,
+            // p = S'^T k, delta = b (v - p), S = S' + k delta^T, o = S^T q
+            // ([K3-explainer] §三/§四).  Lane (l16, l4) holds value column vcol
+            // and key rows 16 t + 4 l4 + e of S; each token's k, q and gates
+            // come straight from global memory.
+            const int m2 = 2 * (tick - 1);
+            const bool mid = m2 + 1 < (int)((tend - tbeg + kBS - 1) / kBS);
+            const int64_t soff = ((tbeg / kBS + n + m2) * H + h) * (int64_t)D * D +
+                                 (int64_t)vcol * D + 4 * l4;
+            auto put_state = [&](int64_t e0) {
+#pragma unroll
+                for (int t = 0; t < G::NRT; ++t) {
+                    if constexpr (sizeof(T) == 2)
+                        *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16 *>(snapshots) + e0 +
+                                                   16 * t) =
+                            u32x2{pack2(Sm[t][0], Sm[t][1]), pack2(Sm[t][2], Sm[t][3])};
+                    else
+                        *reinterpret_cast<f32x4 *>(snapshots + e0 + 16 * t) = Sm[t];
+                }
+            };
+            if constexpr (MODE == kModeStates) put_state(soff);
+            for (int j = 0; j < nvalid; ++j) {
+                const int64_t row = (tok0 + j) * H + h;
+                const T *kr = k + row * D + 4 * l4;
+                const T *qr = q + row * D + 4 * l4;
+                float p = 0.f;
+#pragma unroll
+                for (int t = 0; t < G::NRT; ++t) {
+                    float kf[4], af[4];
+                    load4(kr + 16 * t, kf);
+                    if constexpr (SG) {
+                        const float a = fast_exp2(log_alpha[row] * kLog2e);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) af[e] = a;
+                    } else {
+                        const f32x4 g = *reinterpret_cast<const f32x4 *>(
+                            log_alpha + row * D + 16 * t + 4 * l4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) af[e] = fast_exp2(g[e] * kLog2e);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Sm[t][e] *= af[e];
+                        p += Sm[t][e] * kf[e];
+                    }
+                }
+                p += __shfl_xor(p, 16, 64);
+                p += __shfl_xor(p, 32, 64);
+                const float vv = MODE == kModeMap ? 0.f : to_f32(v[row * D + vcol]);
+                const float dl = beta[row] * (vv - p);
+                float o = 0.f;
+#pragma unroll
+                for (int t = 0; t < G::NRT; ++t) {
+                    float kf[4], qf[4];
+                    load4(kr + 16 * t, kf);
+                    load4(qr + 16 * t, qf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Sm[t][e] += kf[e] * dl;
+                        o += Sm[t][e] * qf[e];
+                    }
+                }
+                if constexpr (MODE == kModeOut) {
+                    o += __shfl_xor(o, 16, 64);
+                    o += __shfl_xor(o, 32, 64);
+                    if (l4 == 0) sO[j * (G::LSV / G::SZ) + 16 * ct + l16] = from_f32<T>(o);
+                }
+                if constexpr (MODE == kModeStates)
+                    if (j == kBS - 1 && mid) put_state(soff + (int64_t)H * D * D);
+            }
+        } else if (on) {
             // the state as B operands, one per contraction block
             typename SM::Frag Sb[D / G::KB];
 #pragma unroll
@@ -911,6 +1053,15 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         __syncthreads();
 
         // ---------------------------------------------------------- phase 2
+        if (FAR && tick < nchunks) {
+            // chunk `tick`, just prepared, is scanned next tick: the
+            // preparation's out-of-range words for it (lane j < 4 PW reads word j)
+            const unsigned fw =
+                lane < 4 * G::PW ? *reinterpret_cast<const unsigned *>(
+                                       smem + (tick & 1) * G::SET + G::flag_offset(lane))
+                                 : 0u;
+            far_next = __ballot(fw != 0u) != 0ull;
+        }
         if (on) {
             // the chunk's O rows (32 x DVS), whole rows in 16-byte pieces
             constexpr int LV = G::RBV / 16;
@@ -925,8 +1076,10 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                             reinterpret_cast<const unsigned char *>(sO) + orow * G::LSV + b);
             }
             // S <- Diag(gamma) S + Diag(f1) (K e^{rho - Gamma})^T Delta
+            // (far chunks: already stepped token by token in phase 1)
             const typename SM::Frag Db0 = SM::b(Dl[0], Dl[1]);
             const typename SM::Frag Db1 = SM::b(Dl[1], Dl[1]);
+            if (!far) {
             if constexpr (MODE == kModeStates) {
                 // the chunk's entering state (block 2 m) and, if the sequence has
                 // a block 2 m + 1, the state after block 0:
@@ -973,6 +1126,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sm[t][e] = gm[e] * Sm[t][e] + f1[e] * acc[e];
             }
+            }
             // a snapshot after every snap_every tokens (a multiple of the chunk
             // length, so only full chunks end on one)
             const int64_t done = (int64_t)tick * kC;
@@ -990,7 +1144,21 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         __syncthreads();
     }
 
-    if (final_state) {
+    bool marked = false;
+    if constexpr (MARK) {
+        // the preparation's sticky out-of-range words of both buffer sets
+        // (their last writes came before the loop's last barrier)
+        marked = __builtin_amdgcn_readfirstlane(
+                     *reinterpret_cast<const unsigned *>(smem + G::sMark) |
+                     *reinterpret_cast<const unsigned *>(smem + G::SET + G::sMark)) != 0u;
+        if (marked && ct == 0 && lane == 0) {
+            if (out)
+                out[(tbeg * H + h) * (int64_t)D + v0] = from_f32<T>(__builtin_nanf(""));
+            else
+                final_state[sbase + (int64_t)v0 * D] = __builtin_nanf("");
+        }
+    }
+    if (final_state && !marked) {
 #pragma unroll
         for (int t = 0; t < G::NRT; ++t)
             *reinterpret_cast<f32x4 *>(final_state + sbase + (int64_t)vcol * D + 16 * t +
@@ -1014,12 +1182,26 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
     static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), log_alpha,  \
         beta, initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,        \
         snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd
-    if (cu_seqlens && num_seqs <= 64)  // packed: longest sequences first
-        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, true>), dim3(8 * per_xcd),
-                           dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, KDA_KERNEL_ARGS);
-    else
-        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, false>), dim3(8 * per_xcd),
-                           dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream, KDA_KERNEL_ARGS);
+    // the fast kernel, then (except for the backward's states mode) the fix-up
+    // pass over the units it marked
+    constexpr bool FIXUP = MODE != kModeStates;
+    if (cu_seqlens && num_seqs <= 64) {  // packed: longest sequences first
+        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, true, false>),
+                           dim3(8 * per_xcd), dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream,
+                           KDA_KERNEL_ARGS);
+        if (FIXUP)
+            hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, true, FIXUP>),
+                               dim3(8 * per_xcd), dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream,
+                               KDA_KERNEL_ARGS);
+    } else {
+        hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, false, false>),
+                           dim3(8 * per_xcd), dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream,
+                           KDA_KERNEL_ARGS);
+        if (FIXUP)
+            hipLaunchKernelGGL((chunk_fwd_kernel<T, D, DVS, SG, MODE, false, FIXUP>),
+                               dim3(8 * per_xcd), dim3(Cfg<T, D, DVS, SG>::THREADS), 0, stream,
+                               KDA_KERNEL_ARGS);
+    }
 #undef KDA_KERNEL_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -45,11 +45,17 @@
  *     num_heads * d_k <= 8388607 (64 tokens of one tensor must span less
  *     than 2^31 bytes).  Other valid sizes return KDA_ERR_UNSUPPORTED.
  *
- * Numerics contract: log_alpha must be finite and, within each run of 16
- * tokens that starts at a multiple of 16 from the sequence start, its sum per
- * channel must stay above -80 (e.g. log_alpha >= -5 everywhere).  The chunked
- * prefill relies on this to keep exp(-decay) within fp32 range; outside it,
- * results may be inf/NaN.  NaN or Inf inputs propagate; they are not trapped.
+ * Gates: every alpha in [0, 1] is accepted, i.e. any log_alpha <= 0
+ * including -inf (alpha = 0), by the prefill and decode entry points.  The
+ * chunked prefill factorises each chunk's products with e^{+-(decay within a
+ * 16-token block)}; a (sequence, head) in which some block decays by more than
+ * 2^-100 in some channel (or has a -inf gate) is recomputed by a second
+ * launch on the same stream, those chunks token by token in fp32 (exact, but
+ * slower for such sequences).  NaN inputs propagate; they are not trapped.
+ * kda_chunk_bwd keeps a narrower contract: log_alpha finite and, within each
+ * run of 16 tokens that starts at a multiple of 16 from the sequence start,
+ * its sum per channel above -80 (e.g. log_alpha >= -5); outside it the
+ * gradients may be inf/NaN.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -164,7 +170,7 @@ int kda_chunk_fwd_snapshots(const void *q, const void *k, const void *v, const f
  *
  * Every argument has the meaning, rules and layout of kda_chunk_fwd except
  *   log_alpha  [B, T, H] fp32 (dense) or [1, T, H] (packed), 4-byte aligned,
- * with the same numerics contract (finite, a 16-token sum above -80).
+ * and the same gate domain (any log_alpha <= 0, -inf included).
  * Returns KDA_OK or a kda_status error code.
  */
 int kda_chunk_fwd_scalar_gate(const void *q, const void *k, const void *v,
@@ -290,8 +296,8 @@ int kda_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
  * unspecified.  No output may overlap an input, another output or
  * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
  * bf16 (bf16 inputs: bf16 matrix products with fp32 accumulation; fp32 inputs:
- * fp32 throughout).  Same numerics contract as
- * kda_chunk_fwd.  Returns KDA_OK or a kda_status error code.
+ * fp32 throughout).  Gates: the backward's narrower contract stated at the
+ * top of this file.  Returns KDA_OK or a kda_status error code.
  */
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,

@@ -218,5 +218,7 @@ def check_prefill_full(inp, out_gpu, fin_gpu, group=16, oracle_fn=None, threads=
         w.add_out(slice_row_errors(_heads_f64(out_gpu, B, T, h0, h1), ref_out, starts))
         if fin_gpu is not None:
             w.add_state(state_errors(f64(fin_gpu[:, h0:h1]), ref_st))
+        if H > group:  # progress of long comparisons
+            print(f"  {label}: heads {h0}..{h1 - 1} done ({w})", flush=True)
     w.check(q.dtype, label)
     return w

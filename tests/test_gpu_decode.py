@@ -88,6 +88,7 @@ def test_decode_full_size_all_units():
         got = f64(out_gpu[:, :, h0:h1].reshape(B * S, h1 - h0, -1))
         worst.add_out(slice_row_errors(got, ref_out, starts))
         worst.add_state(state_errors(f64(fin_gpu[:, h0:h1]), ref_st))
+        print(f"  decode full: heads {h0}..{h1 - 1} done ({worst})", flush=True)
     worst.check(torch.bfloat16, "decode full, all units")
 
 
