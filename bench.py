@@ -31,7 +31,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--backward [--bwd-workload k3_prefill_32k|prefill_4k|varlen_16]]
                               (instead: kda_chunk_bwd, the gradients of the
                                prefill, on its own JSON line)
-       [--prefill-workload tiny|prefill_4k|varlen_16|k3_prefill_32k|long_1m_h96]
+       [--prefill-workload tiny|prefill_4k|prefill_4k_f32|varlen_16|k3_prefill_32k|long_1m_h96]
                               (instead: kda_chunk_fwd alone on that workload, dense
                                or packed; its own JSON line)
        [--segments G [--seg-workload long_1m|prefill_4k]]
@@ -558,8 +558,8 @@ def main():
                     choices=["k3_prefill_32k", "prefill_4k", "varlen_16"],
                     help="the prefill workload --backward runs on")
     ap.add_argument("--prefill-workload", default=None,
-                    choices=["tiny", "prefill_4k", "varlen_16", "k3_prefill_32k",
-                             "long_1m_h96"],
+                    choices=["tiny", "prefill_4k", "prefill_4k_f32", "varlen_16",
+                             "k3_prefill_32k", "long_1m_h96"],
                     help="time kda_chunk_fwd alone on this workload instead (its own JSON line)")
     args = ap.parse_args()
     if args.scalar_gate and args.snapshot_every:

@@ -176,7 +176,6 @@ int chunk_fwd_impl(const void *q, const void *k, const void *v, const float *log
     if (head_dim_k != head_dim_v) return KDA_ERR_UNSUPPORTED;
     const int d = head_dim_k;
     if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
-    if (dtype == kda::kDtypeF32 && d != 64) return KDA_ERR_UNSUPPORTED;
     if (snap && snapshot_every % kda::kChunkTokens != 0) return KDA_ERR_UNSUPPORTED;
     // the kernel addresses 64 tokens of one tensor with 32-bit byte offsets
     if ((int64_t)num_heads * d * 4 * 64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;

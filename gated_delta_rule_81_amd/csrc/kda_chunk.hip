@@ -443,7 +443,6 @@ __device__ __forceinline__ f32x4 mm16<float>(f32x4 acc, const float *A, int ld, 
 //               A 32-token chunk's second block enters
 //               with e^{Gamma_15} S + (K e^{Gamma_15 - Gamma})_{0..15}^T Delta_0,
 //               the block-0 half of the chunk's own transition.
-constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
 // LPT (compile time, packed input with at most 64 sequences): workgroups take
 // the sequences longest first (see below); otherwise in sequence order.
 // FAR (compile time): false = the fast kernel: every chunk through the
@@ -1218,6 +1217,13 @@ int launch_dtype(const void *q, const void *k, const void *v, const float *log_a
     if (dtype == kDtypeBf16)
         return head_dim == 128 ? launch<bf16, 128, 64, SG, MODE>(KDA_LAUNCH_ARGS)
                                : launch<bf16, 64, 64, SG, MODE>(KDA_LAUNCH_ARGS);
+    if (head_dim == 128)  // fp32 operand sets at d = 128 exceed the LDS: the token recurrence
+        return MODE == kModeStates
+                   ? -1
+                   : launch_chunk_seq(q, k, v, log_alpha, beta, initial_state, cu_seqlens, out,
+                                      final_state, snapshots, snapshot_every, num_snapshots,
+                                      num_seqs, seq_len, total_tokens, num_heads, SG ? 1 : 0,
+                                      MODE, stream);
     return launch<float, 64, 16, SG, MODE>(KDA_LAUNCH_ARGS);
 #undef KDA_LAUNCH_ARGS
 }
@@ -1225,7 +1231,9 @@ int launch_dtype(const void *q, const void *k, const void *v, const float *log_a
 }  // namespace
 
 int chunk_fwd_slices(int head_dim, int dtype) {
-    if (dtype == kDtypeBf16) return head_dim / 64;
+    // bf16: 64 value columns per workgroup; fp32: 16 (d = 64), and at d = 128
+    // the token recurrence's 64
+    if (dtype == kDtypeBf16 || head_dim == 128) return head_dim / 64;
     return head_dim / 16;
 }
 

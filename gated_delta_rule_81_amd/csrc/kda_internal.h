@@ -50,6 +50,22 @@ int launch_chunk_states(const void *q, const void *k, const void *v, const float
 // Workgroups the prefill kernel runs per (sequence, head): one per d_v slice.
 int chunk_fwd_slices(int head_dim, int dtype);
 
+// What a prefill launch produces (see chunk_fwd_kernel): outputs, final
+// states and snapshots; final states only; the state transition (identity
+// start, zero values); the backward's per-16-token checkpoints.
+constexpr int kModeOut = 0, kModeState = 1, kModeMap = 2, kModeStates = 3;
+
+// The prefill for fp32 inputs at head_dim 128 as the token recurrence itself
+// (kda_seq.hip): same arguments and results as launch_chunk_fwd for the modes
+// kModeOut (scalar_gate allowed), kModeState and kModeMap.  Returns 0, or -1
+// if the launch failed or the combination is not one of these.
+int launch_chunk_seq(const void *q, const void *k, const void *v, const float *log_alpha,
+                     const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                     void *out, float *final_state, float *snapshots, int32_t snapshot_every,
+                     int32_t num_snapshots, int32_t num_seqs, int32_t seq_len,
+                     int32_t total_tokens, int32_t num_heads, int scalar_gate, int mode,
+                     hipStream_t stream);
+
 // Tokens per chunk of the prefill; snapshot intervals are multiples of it.
 constexpr int kChunkTokens = 32;
 

@@ -54,6 +54,8 @@ WORKLOADS = {
                      notes="B=1 H=2 T=256 d=64 fp32, zero initial state"),
     "prefill_4k": Workload("prefill_4k", heads=32, head_dim=128, dtype="bf16", seed=1,
                            seq_len=4096, notes="B=1 H=32 T=4096 d=128 bf16, zero state"),
+    "prefill_4k_f32": Workload("prefill_4k_f32", heads=32, head_dim=128, dtype="f32", seed=1,
+                               seq_len=4096, notes="B=1 H=32 T=4096 d=128 fp32, zero state"),
     "k3_prefill_32k": Workload("k3_prefill_32k", heads=96, head_dim=128, dtype="bf16",
                                seed=2, seq_len=32768, init_std=0.02,
                                notes="B=1 H=96 T=32768 d=128 bf16, state N(0,0.02)"),

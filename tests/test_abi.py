@@ -114,10 +114,17 @@ def test_chunk_token_count_must_fit_int32():
 
 @pytest.mark.parametrize("kw", [dict(head_dim_k=128, head_dim_v=64), dict(head_dim_k=96,
                                 head_dim_v=96), dict(head_dim_k=256, head_dim_v=256),
-                                dict(dtype=7), dict(dtype=F32)])
+                                dict(dtype=7)])
 def test_chunk_unsupported(kw):
-    # fp32 prefill is implemented for head dim 64 only
     assert call_chunk(**kw) == UNSUP
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_chunk_supported_set(d, dtype):
+    """d_k = d_v in {64, 128} with fp32 or bf16 q/k/v: valid calls reach the
+    device check (no GPU here) or run."""
+    assert call_chunk(dtype=dtype, head_dim_k=d, head_dim_v=d) in (DEVICE, OK)
 
 
 def test_chunk_head_count_bound_for_32bit_offsets():
@@ -227,7 +234,8 @@ def test_snapshots_misaligned_and_aliased():
 
 def test_snapshots_share_the_chunk_fwd_checks():
     assert call_snap(q=None) == NULL
-    assert call_snap(dtype=F32) == UNSUP
+    assert call_snap(head_dim_k=96, head_dim_v=96) == UNSUP
+    assert call_snap(dtype=F32) in (DEVICE, OK)
     assert call_snap(batch=0) == OK
 
 
@@ -465,7 +473,8 @@ def test_chunk_scalar_gate_checks():
     a = chunk_args()
     assert call_chunk_sg() in (DEVICE, OK)
     assert call_chunk_sg(log_alpha=None) == NULL
-    assert call_chunk_sg(dtype=F32) == UNSUP
+    assert call_chunk_sg(dtype=F32) in (DEVICE, OK)
+    assert call_chunk_sg(head_dim_k=96, head_dim_v=96) == UNSUP
     # one float per (token, head): 4-byte alignment suffices
     assert call_chunk_sg(log_alpha=a["log_alpha"] + 4) in (DEVICE, OK)
     assert call_chunk_sg(log_alpha=a["log_alpha"] + 2) == ALIGN
