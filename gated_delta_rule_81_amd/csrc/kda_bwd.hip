@@ -771,9 +771,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             sched_fence();
         }
         // each product in its own accumulator: with bf16 operands the two are
-        // different MFMA shapes (16x16x16 and 16x16x32), and one's result fed
-        // straight in as the other's accumulator has produced wrong values in
-        // two of the four accumulator components when scheduled back to back
+        // different MFMA shapes (16x16x16 and 16x16x32), and the compiler puts
+        // too few wait states between one's result and the other's accumulator
+        // input on gfx950 (half the accumulator rows then read stale values;
+        // tests/hip/mfma_chain.hip); the library never chains the shapes
         const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + (vcol - r), LD, lane);
         if constexpr (PARTS == 1) dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
         f32x4 ddl;

@@ -1,0 +1,41 @@
+"""No kernel of the library chains one bf16 MFMA shape's result into the other
+shape's accumulator too soon (the hazard tests/mfma_hazard.py describes): every
+HIP source is compiled to gfx950 assembly and scanned.  The checker itself is
+checked on the probe tests/hip/mfma_chain.hip, whose two direct chains it must
+find.  CPU only (hipcc cross-compiles)."""
+import os
+import subprocess
+
+import pytest
+
+from mfma_hazard import find_chains
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_81_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip", "-S",
+         "--cuda-device-only"]
+
+pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+
+
+def _asm(src, tmp_path):
+    out = str(tmp_path / (os.path.basename(src) + ".s"))
+    subprocess.run([HIPCC, *FLAGS, src, "-o", out], check=True, capture_output=True)
+    return open(out).read()
+
+
+def test_checker_finds_the_probe_chains(tmp_path):
+    chains = find_chains(_asm(os.path.join(ROOT, "tests", "hip", "mfma_chain.hip"), tmp_path))
+    pairs = {(a, b) for _, _, a, b, _ in chains}
+    assert ("v_mfma_f32_16x16x32_bf16", "v_mfma_f32_16x16x16_bf16") in pairs
+    assert ("v_mfma_f32_16x16x16_bf16", "v_mfma_f32_16x16x32_bf16") in pairs
+    assert len(chains) == 2  # the padded chain is not reported
+
+
+@pytest.mark.parametrize("src", ["kda_chunk.hip", "kda_bwd.hip", "kda_decode.hip",
+                                 "kda_seq.hip", "kda_segment.hip"])
+def test_library_has_no_short_mixed_mfma_chains(src, tmp_path):
+    chains = find_chains(_asm(os.path.join(CSRC, src), tmp_path))
+    assert not chains, chains[:5]
