@@ -25,11 +25,18 @@
 //   dKe = Delta dS_C^T,  dS0 = diag(gam) dS_C + Q+^T dO - K+^T dX,
 //   dG_last = gam * rowsum(S0 * dS_C) + colsum(dKe * Ke),
 //   dQ = dQ+ e^G,  dK = dK+ e^G + dK- e^-G + dKe e^(G_last - G),
-//   dG = dQ+ Q+ + dK+ K+ - dK- K- - dKe Ke  (+ dG_last on the last row),
-//   dlog_alpha = the within-chunk suffix sum of dG.
+//   dlog_alpha[t] = sum_{i >= t} (dO S0^T * Q+ - dX S0^T * K+)[i]
+//                 + sum_{j < t} (dKe * Ke)[j] + gam * rowsum(S0 * dS_C)
+//                 + sum_{i >= t > j} (dM[i][j] Q+[i] + P[i][j] K+[i]) K-[j],
+// i.e. every factor e^{G_a - G_b} (a > b) of the chunk form that alpha_t
+// enters (b < t <= a), weighted by its gradient.  This equals the suffix sum
+// of dG = dQ+ Q+ + dK+ K+ - dK- K- - dKe Ke (+ dG_last on the last row) but
+// adds no pair that cancels, so it keeps its relative precision for strongly
+// decaying gates.
 // A ragged last chunk is padded with zero rows (and zero gates), which add
-// nothing.  16-token chunks keep e^(+-G) within fp32 under the library's
-// numerics contract (a 16-token gate sum above -80).
+// nothing.  16-token chunks keep e^(+-G) within fp32 where no 16-token block
+// decays beyond 2^-100 in a channel; (sequence, head) pairs with such a block
+// (or a -inf gate) are redone token by token afterwards (bwd_seq_kernel).
 //
 // The dS recursion, dS_prev = diag(gam) dS_C + Q+^T dO - K+^T dX, with dX =
 // diag(b) T^T (M^T dO + Ke dS_C), involves no forward state, so the work is
@@ -815,23 +822,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // (the chain's dS products below read only prep's LDS rows and registers)
         if constexpr (GRAD) __syncthreads();
         if constexpr (GRAD) {
+        // (T and T^T are dead from here: their space takes P^T and dM^T)
+        float *sPt = sT, *sDMt = sTt;
         if (w == 0) {  // dA, P = diag(b) dA and the K+K-^T part of db
             const f32x4 ld = PR::template lds_ldst<D>(zero4(), sLm, LD, sDl, LD, lane);
+            f32x4 pc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
                 const float da = r < i ? -ld[e] : 0.f;
-                sP[i * LS + r] = sBeta[i] * da;
+                pc[e] = sBeta[i] * da;
+                sP[i * LS + r] = pc[e];
                 const float pb = row16_sum(da * sBr[i * LS + r]);
                 if (r == 0) sDB[G::W * kBC + i] = pb;
             }
+            *reinterpret_cast<f32x4 *>(sPt + r * LS + 4 * g4) = pc;
         } else if (w == 1) {  // dM = Tril(dO Delta^T)
             const f32x4 od = PR::template lds_ldst<D>(zero4(), sDO, LD, sDl, LD, lane);
+            f32x4 mc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * g4 + e;
-                sDM[i * LS + r] = r <= i ? od[e] : 0.f;
+                mc[e] = r <= i ? od[e] : 0.f;
+                sDM[i * LS + r] = mc[e];
             }
+            *reinterpret_cast<f32x4 *>(sDMt + r * LS + 4 * g4) = mc;
         }
         __syncthreads();
         if (tid < nval) {
@@ -850,7 +865,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         sched_fence();
         const f32x4 xs = PR::lds_reg(zero4(), sDX, LD, Sm, lane);
         sched_fence();
-        float s1 = 0.f, s2 = 0.f;
+        float s1 = 0.f;
         const f32x4 pkm = PR::lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
         const f32x4 dkm = PR::ldst_lds(PR::ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
                                       LS, sKp + 16 * w, LD, lane);
@@ -858,46 +873,84 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         // dKe = Delta dS_C^T and rowsum(S0 * dS_C), from dS_C[k = kcol][v] = sSD[v][kcol]
         const f32x4 dke = PR::lds_col(zero4(), s1, sDl, LD, sSD + kcol, G::LDSD, Sm, lane);
         sched_fence();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s2 += dke[e] * sKe[(4 * g4 + e) * LD + kcol];
         s1 += __shfl_xor(s1, 16, 64);
         s1 += __shfl_xor(s1, 32, 64);
-        s2 += __shfl_xor(s2, 16, 64);
-        s2 += __shfl_xor(s2, 32, 64);
         const float gamk = sGam[kcol];
         const float gl = sG[(kBC - 1) * LD + kcol];
-        float dgm[4];
+        // dlog_alpha[t] = d/d log alpha_t of every factor e^{G_a - G_b} (a > b) of
+        // the chunk form with b < t <= a, summed as such: the pairs (i >= t > j)
+        // of M and A, the rows i >= t of Q+ S0 and K+ S0, the rows j < t of Ke
+        // and gam (a = 16, b = 0), which all carry alpha_t's decay.  (The suffix
+        // sum of dG = dQ+ Q+ + dK+ K+ - dK- K- - dKe Ke is the same sum with
+        // every pair inside the suffix added and taken away again; the pairs on
+        // the diagonal weigh 1 however small alpha_t is, so that form loses all
+        // relative precision where the gates decay strongly.)
+        float suf[4], pre[4], qpv[4], kpv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             const float gm = sG[tok * LD + kcol], eg = __expf(gm);
+            qpv[e] = sQp[tok * LD + kcol];
+            kpv[e] = sKp[tok * LD + kcol];
             const float dkp = pkm[e] - xs[e];
             const float qv = dqp[e] * eg;
             const float kv = dkp * eg + dkm[e] / eg + dke[e] * __expf(gl - gm);
-            dgm[e] = dqp[e] * sQp[tok * LD + kcol] + dkp * sKp[tok * LD + kcol] -
-                     dkm[e] * sKm[tok * LD + kcol] - dke[e] * sKe[tok * LD + kcol];
+            suf[e] = dqs[e] * qpv[e] - xs[e] * kpv[e];
+            pre[e] = dke[e] * sKe[tok * LD + kcol];
             if (tok < nval) {
                 const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + kcol;
                 dq[gi] = from_f32<T>(qv);
                 dk[gi] = from_f32<T>(kv);
             }
         }
-        if (g4 == 3) dgm[3] += gamk * s1 + s2;  // G_last enters through the last row
-        // suffix sums over the 16 rows: within the lane, then over the groups above
-        dgm[2] += dgm[3];
-        dgm[1] += dgm[2];
-        dgm[0] += dgm[1];
-        float above = 0.f;
+        if (g4 == 3) suf[3] += gamk * s1;  // gam: every row of the chunk
+        // suffix sums of suf and exclusive prefix sums of pre over the 16 rows:
+        // within the lane, then over the lane groups above / below
+        suf[2] += suf[3];
+        suf[1] += suf[2];
+        suf[0] += suf[1];
+        float ex[4];
+        ex[0] = 0.f;
+        ex[1] = pre[0];
+        ex[2] = pre[0] + pre[1];
+        ex[3] = ex[2] + pre[2];
+        const float ptot = ex[3] + pre[3];
+        float above = 0.f, below = 0.f;
 #pragma unroll
-        for (int gg = 1; gg < 4; ++gg) {
-            const float tot = __shfl(dgm[0], r + 16 * gg, 64);
-            if (gg > g4) above += tot;
+        for (int gg = 0; gg < 4; ++gg) {
+            const float ts = __shfl(suf[0], r + 16 * gg, 64);
+            const float tp = __shfl(ptot, r + 16 * gg, 64);
+            if (gg > g4) above += ts;
+            if (gg < g4) below += tp;
+        }
+        // the pairs: R_t = sum_{i >= t} (Q+_i Zm_i(t) + K+_i Zp_i(t)) with
+        // Zm_i(t) = sum_{j < t} dM[i][j] K-_j and Zp_i(t) the same with P; this
+        // lane holds rows i = 4 g4 + e, the four lane groups' sums are added
+        float zm[4] = {0.f, 0.f, 0.f, 0.f}, zp[4] = {0.f, 0.f, 0.f, 0.f};
+        float rt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 1; t < kBC; ++t) {
+            const float km = sKm[(t - 1) * LD + kcol];
+            const f32x4 mc = *reinterpret_cast<const f32x4 *>(sDMt + (t - 1) * LS + 4 * g4);
+            const f32x4 pc = *reinterpret_cast<const f32x4 *>(sPt + (t - 1) * LS + 4 * g4);
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                zm[e] += mc[e] * km;
+                zp[e] += pc[e] * km;
+                const float y = qpv[e] * zm[e] + kpv[e] * zp[e];
+                part += 4 * g4 + e >= t ? y : 0.f;
+            }
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if ((t >> 2) == g4) rt[t & 3] = part;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             if (tok < nval)
-                dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] = dgm[e] + above;
+                dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] =
+                    (suf[e] + above) + (ex[e] + below) + rt[e];
         }
         }  // GRAD
         // state gradient before the chunk: Q+^T dO and K+^T dX per key tile, A from
@@ -946,16 +999,25 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
     if (units == 0) return 0;
     const int64_t slots = (int64_t)total_tokens / kBC + num_seqs + 1;
     if (units > (int64_t)1 << 30 || slots * H > (int64_t)1 << 30) return -1;
+    // Units whose gates leave the chunked kernels' range are marked (flag words
+    // after the two regions) and redone token by token at the end.
+    unsigned *far_flags =
+        reinterpret_cast<unsigned *>(ckpt + 2 * slots * H * (int64_t)D * D);
     // The chunk-entering states from the prefill kernel (32-token chunks, all
-    // CUs' worth of parallelism per head as in the forward) where it supports
-    // the configuration; otherwise the chain kernel recomputes them first.
+    // CUs' worth of parallelism per head as in the forward), which also marks
+    // the units, where it supports the configuration; otherwise a detect pass
+    // marks them and the chain kernel recomputes the states first.
     int ready = 0;
     if ((sizeof(T) == 2 || D == 64) && (int64_t)H * D * 4 * 64 <= INT32_MAX) {
         if (launch_chunk_states(q, k, v, log_alpha, beta, initial_state, cu_seqlens, ckpt,
                                 num_seqs, seq_len, total_tokens, H, D,
-                                sizeof(T) == 2 ? kDtypeBf16 : kDtypeF32, stream) != 0)
+                                sizeof(T) == 2 ? kDtypeBf16 : kDtypeF32, far_flags,
+                                stream) != 0)
             return -1;
         ready = 1;
+    } else if (launch_bwd_far_detect(log_alpha, cu_seqlens, num_seqs, seq_len, total_tokens, H,
+                                     D, far_flags, stream) != 0) {
+        return -1;
     }
     float *dckpt = ckpt + slots * H * D * D;  // second region: chunk-end gradients
 #define KDA_BWD_KERNEL_ARGS                                                                    \
@@ -980,15 +1042,21 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
     hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdGrad>), dim3((unsigned)(slots * H)),
                        dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
 #undef KDA_BWD_KERNEL_ARGS
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    if (hipGetLastError() != hipSuccess) return -1;
+    return launch_bwd_seq(q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_out, d_final,
+                          dq, dk, dv, dlog_alpha, dbeta, d_initial, ckpt, far_flags, num_seqs,
+                          seq_len, total_tokens, H, D, sizeof(T) == 2 ? kDtypeBf16 : kDtypeF32,
+                          stream);
 }
 
 }  // namespace
 
 int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
                                    int head_dim) {
-    // two regions of one state per slot and head: entering states, end gradients
-    return 2 * (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim;
+    // two regions of one state per slot and head (entering states, end
+    // gradients), then the out-of-range flag words of every (sequence, head)
+    return 2 * (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim +
+           bwd_far_flag_words(num_seqs, num_heads);
 }
 
 int launch_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,

@@ -462,7 +462,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
     T *__restrict__ out, float *__restrict__ final_state, float *__restrict__ snapshots,
     int snap_every, int snap_cap, int num_seqs, int seq_len, int total_tokens,
-    int H, int units, int units_per_xcd) {
+    int H, int units, int units_per_xcd, unsigned *__restrict__ far_flags) {
     typedef Cfg<T, D, DVS, SG> G;
     typedef Mma<T> M;
     typedef ScanMma<T> SM;
@@ -518,7 +518,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         tend = tbeg + seq_len;
     }
     const int nchunks = (int)((tend - tbeg + kC - 1) / kC);
-    constexpr bool MARK = !FAR && MODE != kModeStates;  // the fast kernel marks far units
+    // the fast kernel marks far units (states mode: for the backward's flags)
+    constexpr bool MARK = !FAR;
     if constexpr (FAR) {
         // the fix-up pass: only units the fast kernel marked (the same
         // element for every thread, so the whole workgroup returns together)
@@ -1150,7 +1151,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         marked = __builtin_amdgcn_readfirstlane(
                      *reinterpret_cast<const unsigned *>(smem + G::sMark) |
                      *reinterpret_cast<const unsigned *>(smem + G::SET + G::sMark)) != 0u;
-        if (marked && ct == 0 && lane == 0) {
+        if constexpr (MODE == kModeStates) {
+            // the (sequence, head)'s 16 flag words: word 0 the mark, the rest 0
+            if (far_flags && v0 == 0 && ct == 0 && lane < 16)
+                far_flags[((int64_t)n * H + h) * 16 + lane] = (lane == 0 && marked) ? 1u : 0u;
+        } else if (marked && ct == 0 && lane == 0) {
             if (out)
                 out[(tbeg * H + h) * (int64_t)D + v0] = from_f32<T>(__builtin_nanf(""));
             else
@@ -1169,7 +1174,7 @@ template <typename T, int D, int DVS, bool SG, int MODE>
 int launch(const void *q, const void *k, const void *v, const float *log_alpha, const float *beta,
            const float *initial_state, const int32_t *cu_seqlens, void *out, float *final_state,
            float *snapshots, int snap_every, int snap_cap, int num_seqs, int seq_len,
-           int total_tokens, int H, hipStream_t stream) {
+           int total_tokens, int H, unsigned *far_flags, hipStream_t stream) {
     const int64_t units64 = (int64_t)num_seqs * H * (D / DVS);
     if (units64 == 0) return 0;
     if (units64 > (int64_t)1 << 30) return -1;
@@ -1180,7 +1185,7 @@ int launch(const void *q, const void *k, const void *v, const float *log_alpha, 
 #define KDA_KERNEL_ARGS                                                                        \
     static_cast<const T *>(q), static_cast<const T *>(k), static_cast<const T *>(v), log_alpha,  \
         beta, initial_state, cu_seqlens, static_cast<T *>(out), final_state, snapshots,        \
-        snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd
+        snap_every, snap_cap, num_seqs, seq_len, total_tokens, H, units, per_xcd, far_flags
     // the fast kernel, then (except for the backward's states mode) the fix-up
     // pass over the units it marked
     constexpr bool FIXUP = MODE != kModeStates;
@@ -1210,10 +1215,11 @@ int launch_dtype(const void *q, const void *k, const void *v, const float *log_a
                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                  void *out, float *final_state, float *snapshots, int snapshot_every,
                  int num_snapshots, int num_seqs, int seq_len, int total_tokens, int num_heads,
-                 int head_dim, int dtype, hipStream_t stream) {
+                 int head_dim, int dtype, hipStream_t stream, unsigned *far_flags = nullptr) {
 #define KDA_LAUNCH_ARGS                                                                        \
     q, k, v, log_alpha, beta, initial_state, cu_seqlens, out, final_state, snapshots,          \
-        snapshot_every, num_snapshots, num_seqs, seq_len, total_tokens, num_heads, stream
+        snapshot_every, num_snapshots, num_seqs, seq_len, total_tokens, num_heads, far_flags,  \
+        stream
     if (dtype == kDtypeBf16)
         return head_dim == 128 ? launch<bf16, 128, 64, SG, MODE>(KDA_LAUNCH_ARGS)
                                : launch<bf16, 64, 64, SG, MODE>(KDA_LAUNCH_ARGS);
@@ -1241,11 +1247,12 @@ int launch_chunk_states(const void *q, const void *k, const void *v, const float
                         const float *beta, const float *initial_state,
                         const int32_t *cu_seqlens, float *states, int32_t num_seqs,
                         int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
-                        int dtype, hipStream_t stream) {
+                        int dtype, unsigned *far_flags, hipStream_t stream) {
     if (dtype != kDtypeBf16 && head_dim != 64) return -1;
     return launch_dtype<false, kModeStates>(q, k, v, log_alpha, beta, initial_state, cu_seqlens,
                                             nullptr, nullptr, states, kC, 0, num_seqs, seq_len,
-                                            total_tokens, num_heads, head_dim, dtype, stream);
+                                            total_tokens, num_heads, head_dim, dtype, stream,
+                                            far_flags);
 }
 
 int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *log_alpha,

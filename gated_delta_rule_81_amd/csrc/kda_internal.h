@@ -39,13 +39,17 @@ int launch_chunk_fwd(const void *q, const void *k, const void *v, const float *l
 // `states` as the chunked backward's checkpoints (slot tbeg / 16 + n + j for
 // block j of sequence n, [slot][H][d_v][d_k]; chunk_bwd_workspace_floats(...)
 // floats), computed by the prefill kernel without outputs.  Sequences as for
-// launch_chunk_fwd.  bf16 at head_dim 64 or 128, fp32 at 64.  Returns 0, or -1
-// if the launch failed or the configuration is not one of these.
+// launch_chunk_fwd.  bf16 at head_dim 64 or 128, fp32 at 64.  far_flags, if
+// not NULL, receives the 16 flag words of every (sequence, head) that
+// launch_bwd_far_detect would write (word 0 nonzero where a 16-token block
+// decays beyond 2^-100 in some channel or has a -inf / NaN gate, the others
+// 0).  Returns 0, or -1 if the launch failed or the configuration is not one
+// of these.
 int launch_chunk_states(const void *q, const void *k, const void *v, const float *log_alpha,
                         const float *beta, const float *initial_state,
                         const int32_t *cu_seqlens, float *states, int32_t num_seqs,
                         int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
-                        int dtype, hipStream_t stream);
+                        int dtype, unsigned *far_flags, hipStream_t stream);
 
 // Workgroups the prefill kernel runs per (sequence, head): one per d_v slice.
 int chunk_fwd_slices(int head_dim, int dtype);
@@ -79,6 +83,26 @@ int launch_segment_bounds(int32_t *cu, int nseg, int seg_len, int total, hipStre
 // from S = 0).  head_dim is 64 or 128.  Returns 0, or -1 if the launch failed.
 int launch_segment_fold(const float *m0, const float *X, const float *Y, float *m_in, int nseg,
                         int H, int head_dim, hipStream_t stream);
+
+// The backward's fallback for (sequence, head) units whose gates leave the
+// chunked backward's range (a 16-token block decaying beyond 2^-100 in some
+// channel, -inf or NaN gates).  launch_bwd_far_detect writes
+// bwd_far_flag_words(N, H) flag words (nonzero: the unit is out of range);
+// launch_bwd_seq, run after the chunked backward on the same stream,
+// recomputes every gradient of the flagged units token by token in fp32 and
+// leaves the others alone; ckpt holds (total_tokens / 16 + N + 1) * H * d^2
+// fp32 values (the chunked backward's first workspace region).
+int64_t bwd_far_flag_words(int64_t num_seqs, int64_t num_heads);
+int launch_bwd_far_detect(const float *log_alpha, const int32_t *cu_seqlens, int32_t num_seqs,
+                          int32_t seq_len, int32_t total_tokens, int32_t num_heads, int head_dim,
+                          unsigned *flags, hipStream_t stream);
+int launch_bwd_seq(const void *q, const void *k, const void *v, const float *log_alpha,
+                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                   const void *d_out, const float *d_final_state, void *dq, void *dk, void *dv,
+                   float *dlog_alpha, float *dbeta, float *d_initial_state, float *ckpt,
+                   const unsigned *flags, int32_t num_seqs, int32_t seq_len,
+                   int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
+                   hipStream_t stream);
 
 // Chunked backward: gradients of the prefill's outputs and final states with
 // respect to q, k, v, log_alpha, beta and the initial states.  Sequences as

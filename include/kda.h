@@ -52,10 +52,11 @@
  * 2^-100 in some channel (or has a -inf gate) is recomputed by a second
  * launch on the same stream, those chunks token by token in fp32 (exact, but
  * slower for such sequences).  NaN inputs propagate; they are not trapped.
- * kda_chunk_bwd keeps a narrower contract: log_alpha finite and, within each
- * run of 16 tokens that starts at a multiple of 16 from the sequence start,
- * its sum per channel above -80 (e.g. log_alpha >= -5); outside it the
- * gradients may be inf/NaN.
+ * kda_chunk_bwd accepts the same domain: a (sequence, head) in which some
+ * 16-token block (counted from the sequence start) decays by more than 2^-100
+ * in some channel, or has a -inf gate, has all its gradients recomputed token
+ * by token in fp32 by a launch after the chunked ones (exact, much slower for
+ * such sequences: it steps each 16-token block again once per token).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 /* Element type of q, k, v and out. */
 enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 };
@@ -292,12 +293,14 @@ int kda_chunk_fwd_segmented_noalloc(const void *q, const void *k, const void *v,
  * workspace: caller-owned device scratch, 16-byte aligned, of at least
  * kda_chunk_bwd_workspace_size(B * T, N, H, d_k) bytes (else KDA_ERR_SHAPE;
  * NULL: KDA_ERR_NULL), holding each 16-token chunk's entering state and the
- * gradient at its end (both in the input dtype); contents on return are
+ * gradient at its end (both in the input dtype) and the flag words; contents on return are
  * unspecified.  No output may overlap an input, another output or
  * the workspace (KDA_ERR_ALIAS).  Supported: d_k == d_v in {64, 128}, fp32 or
  * bf16 (bf16 inputs: bf16 matrix products with fp32 accumulation; fp32 inputs:
- * fp32 throughout).  Gates: the backward's narrower contract stated at the
- * top of this file.  Returns KDA_OK or a kda_status error code.
+ * fp32 throughout).  Gates: any log_alpha <= 0, -inf included, as stated at
+ * the top of this file; a first launch marks the (sequence, head) pairs
+ * outside the chunked range in the workspace's flag words and a last one
+ * recomputes them.  Returns KDA_OK or a kda_status error code.
  */
 int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_alpha,
                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,
@@ -310,7 +313,9 @@ int kda_chunk_bwd(const void *q, const void *k, const void *v, const float *log_
 /*
  * Bytes of workspace kda_chunk_bwd needs for total_tokens = B * T tokens in
  * num_seqs sequences: 2 * (total_tokens / 16 + num_seqs + 1) * num_heads *
- * head_dim^2 * 4.  -1 for negative sizes or head_dim not 64/128.  Host only.
+ * head_dim^2 * 4 (two regions of one state per 16-token slot and head) +
+ * 16 * num_seqs * num_heads * 4 (the out-of-range flag words).  -1 for
+ * negative sizes or head_dim not 64/128.  Host only.
  */
 int64_t kda_chunk_bwd_workspace_size(int32_t total_tokens, int32_t num_seqs, int32_t num_heads,
                                      int32_t head_dim);

@@ -34,8 +34,10 @@ int launch_segment_fold(const float *, const float *, const float *, float *, in
 }
 int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64_t num_heads,
                                    int head_dim) {
-    // two regions of one fp32 state per 16-token slot and head (the library's rule)
-    return 2 * (total_tokens / 16 + num_seqs + 1) * num_heads * head_dim * head_dim;
+    // two regions of one fp32 state per 16-token slot and head, then 16 flag
+    // words per (sequence, head) (the library's rule)
+    return 2 * (total_tokens / 16 + num_seqs + 1) * num_heads * head_dim * head_dim +
+           16 * num_seqs * num_heads;
 }
 int launch_chunk_bwd(const void *, const void *, const void *, const float *, const float *,
                      const float *, const int32_t *, const void *, const float *, void *, void *,

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.kda_abi_version() == 6
+    assert L.kda_abi_version() == 7
     for code in range(-8, 1):
         assert L.kda_status_string(code).decode() not in ("", "unknown status")
     assert L.kda_status_string(12345) == b"unknown status"
@@ -341,7 +341,9 @@ def test_segmented_noalloc_checks():
 # ---------------------------------------------------------------- chunk_bwd
 def test_bwd_workspace_size():
     f = _lib.lib().kda_chunk_bwd_workspace_size
-    assert f(200, 2, 3, 128) == 2 * (200 // 16 + 2 + 1) * 3 * 128 * 128 * 4
+    # two regions of one fp32 state per 16-token slot and head, then 16 flag
+    # words per (sequence, head) marking gates outside the chunked range
+    assert f(200, 2, 3, 128) == 2 * (200 // 16 + 2 + 1) * 3 * 128 * 128 * 4 + 16 * 2 * 3 * 4
     assert f(0, 0, 3, 64) == 2 * 1 * 3 * 64 * 64 * 4
     for bad in [(-1, 1, 1, 64), (10, -1, 1, 64), (10, 1, -1, 64), (10, 1, 1, 96)]:
         assert f(*bad) == -1

@@ -187,3 +187,78 @@ def test_gate_domain_in_place_state_and_selective_fixup():
         for h in range(4):
             if (b, h) != (1, 2):
                 assert torch.equal(out[b, :, h], out_c[b, :, h]) and torch.equal(fin[b, h], fin_c[b, h])
+
+
+# ---------------------------------------------------------------- backward
+# kda_chunk_bwd marks the (sequence, head) units whose gates leave the chunked
+# backward's range (a 16-token block decaying beyond 2^-100 in a channel,
+# -inf or NaN gates) and recomputes all their gradients token by token in fp32
+# after the chunked kernels; the other units keep the chunked results.
+from test_gpu_backward import compare, loss_grads, oracle_grads, packed_parts, run_gpu  # noqa: E402
+
+BWD_KINDS = KINDS + ["one_unit"]
+
+
+def _bwd_gates(g, kind):
+    if kind == "one_unit":  # a single -inf entry: only unit (0, 1) leaves the range
+        g[0, 37, 1, 5] = NEG_INF
+        return g
+    return _gates(g, kind)
+
+
+@pytest.mark.parametrize("kind", BWD_KINDS)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_gate_domain_backward(kind, dtype, d):
+    inp = _case(dtype, d, T=200)
+    _bwd_gates(inp["log_alpha"], kind)
+    d_out, d_fin = loss_grads(inp, 5)
+    say("gate domain backward", kind, dtype, d)
+    g = run_gpu(inp, d_out, d_fin)
+    for name, t in g.items():
+        assert torch.isfinite(t.float()).all(), name
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label=f"bwd gate domain {kind} {dtype} d={d}")
+
+
+def test_gate_domain_backward_selective():
+    """Only unit (sequence 1, head 2) leaves the range: the other units'
+    gradients are bitwise those of a run without the far gates, and repeated
+    runs are bitwise equal."""
+    inp = _case("bf16", 128, T=150, heads=4, batch=3)
+    clean = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    inp["log_alpha"][1, 20:60, 2] = -30.0
+    inp["log_alpha"][1, 100, 2, 9] = NEG_INF
+    d_out, d_fin = loss_grads(inp, 8)
+    say("gate domain backward, one far unit")
+    g = run_gpu(inp, d_out, d_fin)
+    g2 = run_gpu(inp, d_out, d_fin)
+    gc = run_gpu(clean, d_out, d_fin)
+    for name in g:
+        assert torch.equal(g[name], g2[name]), name
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label="bwd gate domain one far unit")
+    for b in range(3):
+        for h in range(4):
+            if (b, h) == (1, 2):
+                continue
+            for name in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+                assert torch.equal(g[name][b, :, h], gc[name][b, :, h]), (name, b, h)
+            assert torch.equal(g["d_initial_state"][b, h], gc["d_initial_state"][b, h])
+
+
+def test_gate_domain_backward_packed():
+    lens = [0, 1, 16, 45, 130, 7, 260]
+    w = synth.WORKLOADS["varlen_16"]
+
+    def make(i, n):
+        p = synth.prefill_inputs(w, n_seqs=0, seq_len=n, heads=2, seed=500 + i)
+        if n > 1:
+            _gates(p["log_alpha"], ["inf_tokens", "minus8_runs", "mixed", "edge_minus4"][i % 4])
+        elif n == 1:
+            p["log_alpha"][:] = NEG_INF
+        return p
+
+    inp = packed_parts(lens, make)
+    d_out, d_fin = loss_grads(inp, 9)
+    say("gate domain backward packed", lens)
+    g = run_gpu(inp, d_out, d_fin)
+    compare(inp, g, oracle_grads(inp, d_out, d_fin), label="bwd gate domain packed")
+    assert torch.equal(g["d_initial_state"][0].cpu(), d_fin[0])

@@ -70,4 +70,4 @@ def test_workspace_size_holds_two_regions():
     f = _lib.lib().kda_chunk_bwd_workspace_size
     for total, n, h, d in [(32768, 1, 96, 128), (4096, 1, 32, 128), (333, 7, 3, 64)]:
         region = (total // CHUNK + n + 1) * h * d * d * 4
-        assert f(total, n, h, d) == 2 * region
+        assert f(total, n, h, d) == 2 * region + 16 * n * h * 4  # + flag words
