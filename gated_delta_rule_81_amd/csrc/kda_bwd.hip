@@ -67,7 +67,7 @@ namespace {
 
 constexpr int kBC = 16;  // tokens per chunk of the backward
 
-template <int D>
+template <int D, bool GRAD>
 struct BwdCfg {
     static constexpr int W = D / 16;  // waves; also 16-wide tiles along d
     static constexpr int THREADS = 64 * W;
@@ -75,28 +75,22 @@ struct BwdCfg {
     static constexpr int LS = 20;      // row stride of 16 x 16 arrays (16-byte rows)
     static constexpr int ROW = kBC * LD;
     static constexpr int SQ = kBC * LS;
+    // lambda (gradient kernel only) takes V's rows: each lane reads its V
+    // entries (for X) before it writes the same entries of lambda
     static constexpr int oQp = 0, oKp = ROW, oKm = 2 * ROW, oKe = 3 * ROW, oG = 4 * ROW,
-                         oV = 5 * ROW, oDO = 6 * ROW, oDl = 7 * ROW, oLm = 8 * ROW,
-                         oDX = 9 * ROW;
+                         oV = 5 * ROW, oDO = 6 * ROW, oDl = 7 * ROW, oLm = oV;
     // P shares A's space (A is dead once T is formed) and dM shares M's (M is
     // last read before the barrier that precedes dM)
-    static constexpr int oBr = 10 * ROW, oA = oBr + SQ, oM = oA + SQ, oT = oM + SQ,
+    static constexpr int oBr = 8 * ROW, oA = oBr + SQ, oM = oA + SQ, oT = oM + SQ,
                          oTt = oT + SQ, oP = oA, oDM = oM;
     static constexpr int oGam = oTt + SQ, oBeta = oGam + D, oDB = oBeta + kBC;
-    // dL/dS at the chunk end, stored [v][k] (the M orientation), for the
-    // products that contract over d_v
-    static constexpr int LDSD = D + 4, oSD = oDB + (W + 1) * kBC;
-    static constexpr int FLOATS = oSD + D * LDSD;
-    // the chain kernel's transposed Q+ and K+ ([D][16], row stride LDT) share the
-    // space of the dL/dS copy, which only the gradient kernel uses
-    static constexpr int LDT = kBC + 4, oQT = oSD, oKT = oSD + D * LDT;
+    static constexpr int oX = oDB + (W + 1) * kBC;
+    // the chain kernel: transposed Q+ and K+ ([D][16], row stride LDT), then
+    // the split chain's partial K_end dS tiles (one f32x4 per lane and wave)
+    static constexpr int LDT = kBC + 4, oQT = oX, oKT = oQT + (GRAD ? 0 : D * LDT),
+                         oXC = oKT + (GRAD ? 0 : D * LDT), XEND = oXC + (GRAD ? 0 : W * 64 * 4);
     // A transposed (column m of A as a row), read by the triangular solve
-    static constexpr int oAt = FLOATS, FLOATS_ALL = oAt + SQ;
-    static_assert(2 * LDT <= LDSD, "transposed rows fit the dL/dS copy's space");
-    // the half-column chain's partial K_end dS tiles (one f32x4 per lane and
-    // wave), after the transposed rows
-    static constexpr int oXC = oKT + D * LDT;
-    static_assert(oXC + W * 64 * 4 <= oSD + D * LDSD, "exchange fits the dL/dS copy's space");
+    static constexpr int oAt = XEND, FLOATS_ALL = oAt + SQ;
 };
 
 __device__ __forceinline__ f32x4 mf(float a, float b, f32x4 c) {
@@ -237,26 +231,6 @@ struct Prod<false> {
                                       int lane) {
         return mm_ldst_tile(acc, At, lda, B, lane);
     }
-    // acc += A (16 x 16NT, row-major) x Bc, where Bc[k][j] = Bs[k * ldb] (a column of a
-    // [k][..] array at this lane's j), and s += sum_k W[k / 16][k % 16 - ...] * Bc[k][j]
-    // with W in register-tile order (row k = 16t + 4g + e); the d_v contraction of
-    // Delta dS^T together with rowsum(S0 * dS).
-    template <int NT>
-    __device__ static f32x4 lds_col(f32x4 acc, float &s, const float *A, int lda, const float *Bs,
-                                    int ldb, const f32x4 (&W)[NT], int lane) {
-        const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(A + r * lda + 16 * t + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float b = Bs[(16 * t + 4 * g + e) * ldb];
-                acc = mf(a[e], b, acc);
-                s += W[t][e] * b;
-            }
-        }
-        return acc;
-    }
 };
 
 template <>
@@ -264,6 +238,7 @@ struct Prod<true> {
     template <int NT>
     __device__ static f32x4 lds_reg(f32x4 acc, const float *A, int lda, const f32x4 (&B)[NT],
                                     int lane) {
+        static_assert(NT % 2 == 0, "bf16 products take register tiles in pairs");
         const int r = lane & 15, g = lane >> 4;
 #pragma unroll
         for (int b = 0; b < NT / 2; ++b) {
@@ -318,26 +293,6 @@ struct Prod<true> {
         return mf16(pack4(a0[0], a0[lda], a0[2 * lda], a0[3 * lda]),
                     pack4(B[0], B[1], B[2], B[3]), acc);
     }
-    template <int NT>
-    __device__ static f32x4 lds_col(f32x4 acc, float &s, const float *A, int lda, const float *Bs,
-                                    int ldb, const f32x4 (&W)[NT], int lane) {
-        const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-        for (int b = 0; b < NT / 2; ++b) {
-            const float *a0 = A + r * lda + 32 * b + 4 * g;
-            f32x4 c0, c1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c0[e] = Bs[(32 * b + 4 * g + e) * ldb];
-                c1[e] = Bs[(32 * b + 16 + 4 * g + e) * ldb];
-                s += W[2 * b][e] * c0[e] + W[2 * b + 1][e] * c1[e];
-            }
-            acc = mf32(pack8(*reinterpret_cast<const f32x4 *>(a0),
-                             *reinterpret_cast<const f32x4 *>(a0 + 16)),
-                       pack8(c0, c1), acc);
-        }
-        return acc;
-    }
 };
 
 // Every lane of a group of 4 receives x from lane SRC of its group (DPP
@@ -364,8 +319,10 @@ __device__ __forceinline__ void ckpt_store(float *base, int64_t off, const f32x4
         *reinterpret_cast<f32x4 *>(base + off) = x;
     }
 }
-template <typename T>
-__device__ __forceinline__ f32x4 ckpt_load4(const float *base, int64_t off) {
+// (offsets of any integer type: an unsigned one lets the compiler address a
+// uniform base plus a 32-bit lane offset)
+template <typename T, typename I>
+__device__ __forceinline__ f32x4 ckpt_load4(const float *base, I off) {
     if constexpr (sizeof(T) == 2) {
         const bf16x4 h =
             *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(base) + off);
@@ -375,12 +332,20 @@ __device__ __forceinline__ f32x4 ckpt_load4(const float *base, int64_t off) {
         return *reinterpret_cast<const f32x4 *>(base + off);
     }
 }
-template <typename T>
-__device__ __forceinline__ float ckpt_load1(const float *base, int64_t off) {
+template <typename T, typename I>
+__device__ __forceinline__ float ckpt_load1(const float *base, I off) {
     if constexpr (sizeof(T) == 2)
         return static_cast<float>(reinterpret_cast<const bf16 *>(base)[off]);
     else
         return base[off];
+}
+
+// base advanced by off elements of T (bf16 or fp32 checkpoints)
+template <typename T>
+__device__ __forceinline__ const float *ckpt_at(const float *base, int64_t off) {
+    return sizeof(T) == 2
+               ? reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(base) + off)
+               : base + off;
 }
 
 // Keeps the scheduler from hoisting the LDS reads of later products above
@@ -431,8 +396,15 @@ template <> struct RawIn<float> {
 // end gradient (`dckpt`), independently of all other chunks.
 constexpr int kBwdChain = 1, kBwdGrad = 2, kBwdChainHalf = 3, kBwdChainQuarter = 4;
 
+// The gradient kernel's LDS (76 KiB at d = 128) lets two workgroups share a
+// CU; its registers are held to that too (4 waves per SIMD at d = 128).
+template <int D, int BMODE>
+constexpr int bwd_min_waves_per_simd() {
+    return BMODE == kBwdGrad ? 2 * (D / 16) / 4 : 1;
+}
+
 template <typename T, int D, int BMODE>
-__global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
+__global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())) void chunk_bwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ log_alpha, const float *__restrict__ beta,
     const float *__restrict__ initial_state, const int32_t *__restrict__ cu_seqlens,
@@ -441,16 +413,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
     float *__restrict__ dbeta, float *__restrict__ d_initial, float *__restrict__ ckpt,
     float *__restrict__ dckpt, int num_seqs, int seq_len, int total_tokens, int H,
     int states_ready) {
-    typedef BwdCfg<D> G;
+    typedef BwdCfg<D, BMODE == kBwdGrad> G;
     typedef Prod<sizeof(T) == 2> PR;  // bf16 inputs: bf16 products, fp32 accumulation
     constexpr int NT = D / 16, LD = G::LD, LS = G::LS;
     __shared__ __attribute__((aligned(16))) float sm[G::FLOATS_ALL];
     float *sQp = sm + G::oQp, *sKp = sm + G::oKp, *sKm = sm + G::oKm, *sKe = sm + G::oKe;
     float *sG = sm + G::oG, *sV = sm + G::oV, *sDO = sm + G::oDO, *sDl = sm + G::oDl;
-    float *sLm = sm + G::oLm, *sDX = sm + G::oDX, *sBr = sm + G::oBr;
+    float *sLm = sm + G::oLm, *sBr = sm + G::oBr;
     float *sM = sm + G::oM, *sT = sm + G::oT, *sTt = sm + G::oTt, *sP = sm + G::oP;
     float *sDM = sm + G::oDM, *sGam = sm + G::oGam, *sBeta = sm + G::oBeta, *sDB = sm + G::oDB;
-    float *sSD = sm + G::oSD, *sAt = sm + G::oAt;
+    float *sAt = sm + G::oAt;
     float *sQT = sm + G::oQT, *sKT = sm + G::oKT;  // chain kernel only
     // the split chain: workgroups per (sequence, head) and key tiles per wave
     constexpr int PARTS = BMODE == kBwdChainHalf ? 2 : BMODE == kBwdChainQuarter ? 4 : 1;
@@ -527,6 +499,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
                                                  ((tbeg / kBC + n) * H + h) * DD)
                      : dckpt + ((tbeg / kBC + n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
+    const unsigned HD = (unsigned)H * D;  // elements between two tokens' rows
     const int64_t sbase = ((int64_t)n * H + h) * DD;
     // S orientation: this lane's value column (the split chain: value group
     // w % VG of value part vpart)
@@ -545,14 +518,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
         const int tok = tid / (D / 4), ch = 4 * (tid % (D / 4));
         const bool ok = tok < nval;
-        const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + ch;
+        const int64_t rb = (t0 * H + h) * (int64_t)D;  // the chunk's first row
+        const unsigned li = (unsigned)tok * HD + ch;
         RawIn<T> R;
-        R.q = with_grad && ok ? RawIn<T>::ld(q + gi) : RawIn<T>::zero();
-        R.k = ok ? RawIn<T>::ld(k + gi) : RawIn<T>::zero();
-        R.v = with_v && ok ? RawIn<T>::ld(v + gi) : RawIn<T>::zero();
-        R.g = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + gi) : zero4();
-        R.o = with_grad && ok ? RawIn<T>::ld(d_out + gi) : RawIn<T>::zero();
-        R.b = tid < kBC && tid < nval ? beta[(t0 + tid) * H + h] : 0.f;
+        R.q = with_grad && ok ? RawIn<T>::ld(q + rb + li) : RawIn<T>::zero();
+        R.k = ok ? RawIn<T>::ld(k + rb + li) : RawIn<T>::zero();
+        R.v = with_v && ok ? RawIn<T>::ld(v + rb + li) : RawIn<T>::zero();
+        R.g = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + rb + li) : zero4();
+        R.o = with_grad && ok ? RawIn<T>::ld(d_out + rb + li) : RawIn<T>::zero();
+        R.b = tid < kBC && tid < nval ? (beta + t0 * H + h)[(unsigned)tid * H] : 0.f;
         return R;
     };
     // `late` runs in every wave after its share of the 16 x 16 work, before the
@@ -731,27 +705,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             for (int t = 0; t < NTW; ++t)
                 ckpt_store<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * (kh * NTW + t) + 4 * g4,
                               dSs[t]);
-        } else {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                dSs[t] = ckpt_load4<T>(dck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4);
         }
-        // dS_C into LDS as [v][k] for the d_v contractions below (the staging's
-        // barriers separate these writes from those reads)
-#pragma unroll
-        for (int t = 0; t < NTW && GRAD; ++t)
-            *reinterpret_cast<f32x4 *>(sSD + vcol * G::LDSD + 16 * t + 4 * g4) = dSs[t];
-        // the chunk's entering state in both orientations, loaded before the
-        // staging so that the two sets of loads are in flight together
         const int64_t s0 = c * ck_stride;  // element offset of S0 in the checkpoints
-        f32x4 Sm[NT];  // [v = 16j + 4g + e][k = kcol]
-#pragma unroll
-        for (int t = 0; t < NT && GRAD; ++t) {
-            Ss[t] = ckpt_load4<T>(ck, s0 + (int64_t)vcol * D + 16 * t + 4 * g4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                Sm[t][e] = ckpt_load1<T>(ck, s0 + (int64_t)(16 * t + 4 * g4 + e) * D + kcol);
-        }
         // the split chain's K_end dS partial (K_end is staged before the 16 x 16
         // work), published for the partner waves before prep's closing barrier
         f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
@@ -763,6 +718,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             }
         });
         const int64_t t0 = tbeg + (int64_t)c * kBC;
+        // the gradient kernel: the chunk's entering state and end gradient in
+        // the S orientation, loaded after the staging (whose triangular solve
+        // needs the registers; the CU's other workgroup covers the latency)
+        const float *ckc = ckpt_at<T>(ck, s0), *dckc = ckpt_at<T>(dck, s0);
+#pragma unroll
+        for (int t = 0; t < NT && GRAD; ++t) {
+            Ss[t] = ckpt_load4<T>(ckc, (unsigned)(vcol * D + 16 * t + 4 * g4));
+            dSs[t] = ckpt_load4<T>(dckc, (unsigned)(vcol * D + 16 * t + 4 * g4));
+        }
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
         f32x4 x = zero4(), dl = zero4();
         if constexpr (GRAD) {
@@ -810,11 +774,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             const int tok = 4 * g4 + e;
             const float dx = sBeta[tok] * lam[e];
             dxr[e] = dx;
-            if constexpr (GRAD) sDX[tok * LD + vcol] = dx;
             if constexpr (GRAD) {
                 sDl[tok * LD + vcol] = dl[e];
                 sLm[tok * LD + vcol] = lam[e];
-                if (tok < nval) dv[((t0 + tok) * H + h) * (int64_t)D + vcol] = from_f32<T>(dx);
+                if (tok < nval) (dv + (t0 * H + h) * D)[(unsigned)tok * HD + vcol] = from_f32<T>(dx);
                 const float pb = row16_sum(x[e] * lam[e]);
                 if (r == 0) sDB[w * kBC + tok] = pb;
             }
@@ -853,25 +816,47 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             float s = 0.f;
 #pragma unroll
             for (int ww = 0; ww <= G::W; ++ww) s += sDB[ww * kBC + tid];
-            dbeta[(t0 + tid) * H + h] = s;
+            (dbeta + t0 * H + h)[(unsigned)tid * H] = s;
         }
-        // key-column products (this wave's 16 key columns), with S0 in M orientation
+        // key-column products (this wave's 16 key columns) that contract over
+        // d_v, with S0 and dS_C in the M orientation ([v = 16j + 4g + e][k =
+        // kcol]) read from the checkpoints 32 rows of v at a time (registers for
+        // two workgroups per CU): dO S0^T, lam S0^T, dKe = Delta dS_C^T and
+        // rowsum(S0 * dS_C)
+        f32x4 dqs = zero4(), xs = zero4(), dke = zero4();
+        float s1 = 0.f;
+#pragma unroll
+        for (int hv = 0; hv < NT / 2; ++hv) {
+            constexpr int NH = 2;  // tiles per step (a bf16 product's pair)
+            f32x4 Sm[NH], dSm[NH];
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned off = (unsigned)((16 * (NH * hv + t) + 4 * g4 + e) * D + kcol);
+                    Sm[t][e] = ckpt_load1<T>(ckc, off);
+                    dSm[t][e] = ckpt_load1<T>(dckc, off);
+                }
+            dqs = PR::lds_reg(dqs, sDO + 16 * NH * hv, LD, Sm, lane);
+            xs = PR::lds_reg(xs, sLm + 16 * NH * hv, LD, Sm, lane);
+            dke = PR::lds_reg(dke, sDl + 16 * NH * hv, LD, dSm, lane);
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s1 += Sm[t][e] * dSm[t][e];
+            sched_fence();
+        }
         // (separate accumulators for the two MFMA shapes, as for ddl above)
-        const f32x4 dqs = PR::lds_reg(zero4(), sDO, LD, Sm, lane);
         const f32x4 dqm = PR::lds_lds(zero4(), sDM, LS, sKm + 16 * w, LD, lane);
         f32x4 dqp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dqp[e] = dqs[e] + dqm[e];
-        sched_fence();
-        const f32x4 xs = PR::lds_reg(zero4(), sDX, LD, Sm, lane);
-        sched_fence();
-        float s1 = 0.f;
+        // dX S0^T = diag(b) (lam S0^T)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[e] *= sBeta[4 * g4 + e];
         const f32x4 pkm = PR::lds_lds(zero4(), sP, LS, sKm + 16 * w, LD, lane);
         const f32x4 dkm = PR::ldst_lds(PR::ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
                                       LS, sKp + 16 * w, LD, lane);
-        sched_fence();
-        // dKe = Delta dS_C^T and rowsum(S0 * dS_C), from dS_C[k = kcol][v] = sSD[v][kcol]
-        const f32x4 dke = PR::lds_col(zero4(), s1, sDl, LD, sSD + kcol, G::LDSD, Sm, lane);
         sched_fence();
         s1 += __shfl_xor(s1, 16, 64);
         s1 += __shfl_xor(s1, 32, 64);
@@ -898,9 +883,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
             suf[e] = dqs[e] * qpv[e] - xs[e] * kpv[e];
             pre[e] = dke[e] * sKe[tok * LD + kcol];
             if (tok < nval) {
-                const int64_t gi = ((t0 + tok) * H + h) * (int64_t)D + kcol;
-                dq[gi] = from_f32<T>(qv);
-                dk[gi] = from_f32<T>(kv);
+                const unsigned gi = (unsigned)tok * HD + kcol;
+                (dq + (t0 * H + h) * D)[gi] = from_f32<T>(qv);
+                (dk + (t0 * H + h) * D)[gi] = from_f32<T>(kv);
             }
         }
         if (g4 == 3) suf[3] += gamk * s1;  // gam: every row of the chunk
@@ -949,7 +934,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void chunk_bwd_kernel(
         for (int e = 0; e < 4; ++e) {
             const int tok = 4 * g4 + e;
             if (tok < nval)
-                dlog_alpha[((t0 + tok) * H + h) * (int64_t)D + kcol] =
+                (dlog_alpha + (t0 * H + h) * D)[(unsigned)tok * HD + kcol] =
                     (suf[e] + above) + (ex[e] + below) + rt[e];
         }
         }  // GRAD
@@ -1030,17 +1015,17 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
     // four at d = 128 when four per pair still fit on the device's CUs
     if (D == 128 && ready && 4 * units <= device_cus())
         hipLaunchKernelGGL((chunk_bwd_kernel<T, D, D == 128 ? kBwdChainQuarter : kBwdChainHalf>),
-                           dim3((unsigned)(4 * units)), dim3(BwdCfg<D>::THREADS), 0, stream,
+                           dim3((unsigned)(4 * units)), dim3(BwdCfg<D, false>::THREADS), 0, stream,
                            KDA_BWD_KERNEL_ARGS);
     else if (ready)
         hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChainHalf>), dim3((unsigned)(2 * units)),
-                           dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+                           dim3(BwdCfg<D, false>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
     else
         hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdChain>), dim3((unsigned)units),
-                           dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+                           dim3(BwdCfg<D, false>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
     if (hipGetLastError() != hipSuccess) return -1;
     hipLaunchKernelGGL((chunk_bwd_kernel<T, D, kBwdGrad>), dim3((unsigned)(slots * H)),
-                       dim3(BwdCfg<D>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
+                       dim3(BwdCfg<D, false>::THREADS), 0, stream, KDA_BWD_KERNEL_ARGS);
 #undef KDA_BWD_KERNEL_ARGS
     if (hipGetLastError() != hipSuccess) return -1;
     return launch_bwd_seq(q, k, v, log_alpha, beta, initial_state, cu_seqlens, d_out, d_final,
