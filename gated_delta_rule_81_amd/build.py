@@ -23,7 +23,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_seq.hip", "kda_segment.hip",
-           "kda_bwd.hip"]
+           "kda_bwd.hip", "kda_bwd_chain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-mcode-object-version=5",

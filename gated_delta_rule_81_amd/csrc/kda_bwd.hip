@@ -1013,7 +1013,12 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
     // the chain: two workgroups per (sequence, head), one per value half, when
     // the states are ready (the pass that computes them runs on whole heads);
     // four at d = 128 when four per pair still fit on the device's CUs
-    if (D == 128 && ready && 4 * units <= device_cus())
+    if (sizeof(T) == 2 && ready) {
+        // bf16: the pipelined chain (preparation one chunk ahead of the scan)
+        if (launch_bwd_chain(q, k, log_alpha, beta, cu_seqlens, d_out, d_final, d_initial, dckpt,
+                             num_seqs, seq_len, total_tokens, H, D, stream) != 0)
+            return -1;
+    } else if (D == 128 && ready && 4 * units <= device_cus())
         hipLaunchKernelGGL((chunk_bwd_kernel<T, D, D == 128 ? kBwdChainQuarter : kBwdChainHalf>),
                            dim3((unsigned)(4 * units)), dim3(BwdCfg<D, false>::THREADS), 0, stream,
                            KDA_BWD_KERNEL_ARGS);

@@ -1,0 +1,391 @@
+// kda_bwd_chain.hip -- the backward's dL/dS chain for bf16 inputs, pipelined.
+//
+// Pages cited (by title):
+//   [K3-explainer]  lshu.cn news 263999, the Kimi K3 explainer (§四: the KDA
+//                   update; §六.2: a chunk's updates as matrix products).
+//
+// The chunk form of the forward (per 16-token chunk with entering state S0,
+// Gamma = the within-chunk prefix of log_alpha, K+ = K e^G, K- = K e^-G,
+// Q+ = Q e^G, Ke = K e^(G_last - G), gam = e^G_last, A = StrictTril(diag(b)
+// K+ K-^T), M = Tril(Q+ K-^T), T = (I + A)^-1) carries dL/dS backwards over
+// the chunks with
+//   dS_prev = diag(gam) dS + Q+^T dO - K+^T dX,
+//   dX = diag(b) T^T (M^T dO + Ke dS),
+// which needs no forward state.  Everything in it except the products with dS
+// is fixed by the chunk's inputs, so it is split the way the prefill splits
+// its chunk recurrence: preparation waves form, one chunk ahead, the operands
+// of a chunk (Ke, K+^T, Q+^T, dO^T, T^T, gam, b and M^T dO) in one of two LDS
+// operand sets, while the scan waves carry dS through the previous chunk from
+// the other set:
+//   ddl = M^T dO + Ke dS        (dS in registers, Ke from the set)
+//   lam = T^T ddl,  dX = b lam  (register tiles feed the next product)
+//   dS  = diag(gam) dS + Q+^T dO - K+^T dX.
+// Two barriers per chunk.  One workgroup per (sequence, head, half of the
+// value columns); the scan waves hold 16 value columns each, all d_k rows, as
+// fp32 registers.  Before a chunk is processed its dS (the gradient at the
+// chunk's end) is written to the checkpoint slot the gradient kernel reads;
+// after the first chunk dS is the initial state's gradient.  bf16 matrix
+// products with fp32 accumulation throughout (v_mfma_f32_16x16x32_bf16 for the
+// d_k contractions, 16x16x16 for the 16-token ones; never one shape's result
+// as the other's accumulator).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kCC = 16;  // tokens per chunk
+
+template <int D>
+struct ChainCfg {
+    static constexpr int DV = D / 2;     // value columns per workgroup
+    static constexpr int PW = D / 16;    // preparation waves: (channel, 4 tokens) per thread
+    static constexpr int SW = DV / 16;   // scan waves: 16 value columns each
+    static constexpr int THREADS = 64 * (PW + SW);
+    static constexpr int NT = D / 16;    // 16-row key tiles of a scan lane's state
+    static constexpr int LR = D + 8;     // bf16 row stride of [16][D] arrays
+    static constexpr int LT = 24;        // bf16 row stride of [x][16 tokens] arrays
+    // one operand set (byte offsets)
+    static constexpr int oKe = 0;                       // Ke [16][LR]
+    static constexpr int oKpT = oKe + 16 * LR * 2;      // K+^T [D][LT]
+    static constexpr int oQpT = oKpT + D * LT * 2;      // Q+^T [D][LT]
+    static constexpr int oDOT = oQpT + D * LT * 2;      // dO^T [DV][LT] (this half)
+    static constexpr int oTt = oDOT + DV * LT * 2;      // T^T [16][LT]
+    static constexpr int oDM = oTt + 16 * LT * 2;       // M^T dO, [SW][64 lanes] f32x4
+    static constexpr int oGam = oDM + SW * 64 * 16;     // gam [D] fp32
+    static constexpr int oBeta = oGam + D * 4;          // b [16] fp32
+    static constexpr int SET = oBeta + 16 * 4;
+    // the preparation's own rows (one copy): K+, K-, Q+ [16][LR] bf16, A^T fp32
+    static constexpr int oKp = 2 * SET, oKm = oKp + 16 * LR * 2, oQp = oKm + 16 * LR * 2;
+    static constexpr int LA = 20;                       // fp32 row stride of A^T
+    static constexpr int oAt = oQp + 16 * LR * 2;
+    static constexpr int BYTES = oAt + 16 * LA * 4;
+    static_assert(SET % 16 == 0 && oAt % 16 == 0, "16-byte aligned arrays");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// 8 bf16 of a row with k contiguous: k = 32 b + 4 g + e and 32 b + 16 + 4 g + e
+// (the 16x16x32 operand of lane group g)
+__device__ __forceinline__ bf16x8 row8(const bf16 *row, int b, int g) {
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + 32 * b + 4 * g);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 32 * b + 16 + 4 * g);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+// 4 bf16 of a row: k = 4 g + e (the 16x16x16 operand of lane group g)
+__device__ __forceinline__ i16x4 row4(const bf16 *row, int g) {
+    return __builtin_bit_cast(i16x4, *reinterpret_cast<const u32x2 *>(row + 4 * g));
+}
+__device__ __forceinline__ i16x4 pk4(const f32x4 &x) {
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = static_cast<bf16>(x[e]);
+    return __builtin_bit_cast(i16x4, r);
+}
+__device__ __forceinline__ bf16x8 pk8(const f32x4 &a, const f32x4 &b) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = static_cast<bf16>(a[e]);
+        r[4 + e] = static_cast<bf16>(b[e]);
+    }
+    return r;
+}
+__device__ __forceinline__ f32x4 mma32(const bf16x8 &a, const bf16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const i16x4 &a, const i16x4 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+template <int SRC>
+__device__ __forceinline__ float quad_from(float x) {  // lane SRC of each group of 4
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), SRC * 0x55, 0xf, 0xf, false));
+}
+
+template <int D>
+__global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const float *__restrict__ log_alpha,
+    const float *__restrict__ beta, const int32_t *__restrict__ cu_seqlens,
+    const bf16 *__restrict__ d_out, const float *__restrict__ d_final,
+    float *__restrict__ d_initial, bf16 *__restrict__ dckpt, int num_seqs, int seq_len,
+    int total_tokens, int H, int units, int units_per_xcd) {
+    typedef ChainCfg<D> G;
+    constexpr int NT = G::NT, LR = G::LR, LT = G::LT;
+    __shared__ __attribute__((aligned(16))) unsigned char sm[G::BYTES];
+
+    // workgroup -> (unit, value half): the units of an XCD are contiguous and
+    // both halves of a unit run on the same XCD (shared chunk inputs in L2)
+    const int bid = blockIdx.x, kx = bid >> 3;
+    const int unit = (bid & 7) * units_per_xcd + (kx >> 1), half = kx & 1;
+    if (unit >= units) return;
+    const int h = unit % H;
+    int n = unit / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // role branches: uniform
+    const int r = lane & 15, g4 = lane >> 4;
+    if (cu_seqlens && num_seqs <= 64) {
+        // packed: the chains of the longest sequences first (position n takes
+        // the sequence of rank n by clamped length, ties by index)
+        int len = -1;
+        if (lane < num_seqs) {
+            int a = cu_seqlens[lane], b = cu_seqlens[lane + 1];
+            a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+            b = b < a ? a : (b > total_tokens ? total_tokens : b);
+            len = b - a;
+        }
+        int rank = 0;
+        for (int m = 0; m < num_seqs; ++m) {
+            const int lm = __builtin_amdgcn_readlane(len, m);
+            rank += (lm > len || (lm == len && m < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < num_seqs && rank == n);
+        n = __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+    }
+    int64_t tbeg, tend;
+    if (cu_seqlens) {
+        int a = cu_seqlens[n], b = cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+        b = b < a ? a : (b > total_tokens ? total_tokens : b);
+        tbeg = a, tend = b;
+    } else {
+        tbeg = (int64_t)n * seq_len, tend = tbeg + seq_len;
+    }
+    const int nch = (int)((tend - tbeg + kCC - 1) / kCC);
+    const int64_t DD = (int64_t)D * D;
+    const unsigned HD = (unsigned)H * D;
+    const int64_t sbase = ((int64_t)n * H + h) * DD;
+    // chunk c's end gradient goes to slot tbeg / 16 + n + c ([slot][H][d_v][d_k])
+    bf16 *dck = dckpt + ((tbeg / kCC + n) * H + h) * DD;
+    const int64_t ck_stride = (int64_t)H * DD;
+    auto set_at = [&](int s) { return sm + s * G::SET; };
+
+    if (wave < G::PW) {
+        // ======================================================== preparation
+        // thread (channel ch, token quarter tq) for the elementwise work;
+        // (value column dv, token quarter dq) for the dO rows of this half
+        const int ch = 16 * wave + r, tq = g4;
+        const int dv = tid % G::DV, dq = tid / G::DV;
+        const bool has_o = tid < 4 * G::DV;
+        float rg[4], rb = 0.f;
+        bf16 rk[4], rq[4], ro[4];
+        auto load = [&](int c) {
+            const int64_t t0 = tbeg + (int64_t)c * kCC;
+            const int nv = (int)((tend - t0) < kCC ? (tend - t0) : kCC);
+            const int64_t row0 = (t0 * H + h) * (int64_t)D;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * tq + j;
+                const unsigned off = (unsigned)i * HD + ch;
+                const bool ok = i < nv;
+                rg[j] = ok ? log_alpha[row0 + off] : 0.f;
+                rk[j] = ok ? k[row0 + off] : static_cast<bf16>(0.f);
+                rq[j] = ok ? q[row0 + off] : static_cast<bf16>(0.f);
+                const int io = 4 * dq + j;
+                ro[j] = has_o && io < nv ? d_out[row0 + (unsigned)io * HD + half * G::DV + dv]
+                                         : static_cast<bf16>(0.f);
+            }
+            rb = tid < kCC && tid < nv ? beta[(t0 + tid) * H + h] : 0.f;
+        };
+        if (nch > 0) load(nch - 1);
+        for (int tick = 0; tick <= nch && nch > 0; ++tick) {
+            const int c = nch - 1 - tick;  // the chunk prepared in this tick
+            unsigned char *S = set_at(tick & 1);
+            if (c >= 0) {
+                // ---- phase 1: prefix, exponentials, the operand rows
+                float pre[4], acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc += rg[j];
+                    pre[j] = acc;
+                }
+                const float s0 = __shfl(acc, r, 64), s1 = __shfl(acc, r + 16, 64);
+                const float s2 = __shfl(acc, r + 32, 64), s3 = __shfl(acc, r + 48, 64);
+                const float off = tq == 0 ? 0.f : tq == 1 ? s0 : tq == 2 ? s0 + s1 : (s0 + s1) + s2;
+                const float glast = ((s0 + s1) + s2) + s3;
+                bf16 kp[4], qp[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * tq + j;
+                    const float gi = off + pre[j];
+                    const float eg = __expf(gi), kv = static_cast<float>(rk[j]);
+                    kp[j] = static_cast<bf16>(kv * eg);
+                    qp[j] = static_cast<bf16>(static_cast<float>(rq[j]) * eg);
+                    reinterpret_cast<bf16 *>(sm + G::oKp)[i * LR + ch] = kp[j];
+                    reinterpret_cast<bf16 *>(sm + G::oKm)[i * LR + ch] =
+                        static_cast<bf16>(kv * __expf(-gi));
+                    reinterpret_cast<bf16 *>(sm + G::oQp)[i * LR + ch] = qp[j];
+                    reinterpret_cast<bf16 *>(S + G::oKe)[i * LR + ch] =
+                        static_cast<bf16>(kv * __expf(glast - gi));
+                }
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(S + G::oKpT) + ch * LT +
+                                            4 * tq) = bf16x4{kp[0], kp[1], kp[2], kp[3]};
+                *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(S + G::oQpT) + ch * LT +
+                                            4 * tq) = bf16x4{qp[0], qp[1], qp[2], qp[3]};
+                if (tq == 0) reinterpret_cast<float *>(S + G::oGam)[ch] = __expf(glast);
+                if (has_o)
+                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(S + G::oDOT) + dv * LT +
+                                                4 * dq) = bf16x4{ro[0], ro[1], ro[2], ro[3]};
+                if (tid < kCC) reinterpret_cast<float *>(S + G::oBeta)[tid] = rb;
+            }
+            __syncthreads();  // A
+            if (c >= 0) {
+                // ---- phase 2: the 16 x 16 work; the next chunk's rows
+                if (c > 0) load(c - 1);
+                const bf16 *kpr = reinterpret_cast<const bf16 *>(sm + G::oKp) + r * LR;
+                const bf16 *kmr = reinterpret_cast<const bf16 *>(sm + G::oKm) + r * LR;
+                const bf16 *qpr = reinterpret_cast<const bf16 *>(sm + G::oQp) + r * LR;
+                if (wave == 0) {
+                    // A = diag(b) StrictTril(K+ K-^T): lane (column r, rows 4 g4 + e)
+                    f32x4 a = zero4();
+#pragma unroll
+                    for (int b = 0; b < D / 32; ++b) a = mma32(row8(kpr, b, g4), row8(kmr, b, g4), a);
+                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(
+                        reinterpret_cast<const float *>(S + G::oBeta) + 4 * g4);
+                    float *at = reinterpret_cast<float *>(sm + G::oAt);
+                    f32x4 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) av[e] = 4 * g4 + e > r ? bt[e] * a[e] : 0.f;
+                    *reinterpret_cast<f32x4 *>(at + r * G::LA + 4 * g4) = av;  // A^T row r
+                    wave_lds_fence();
+                    // T = (I + A)^-1 by right-looking substitution: lane 4 j + qd holds
+                    // rows 4 qd .. 4 qd + 3 of column j; at step m the pivot T[m][j]
+                    // comes from quad lane m / 4, and every row below m takes
+                    // -A[row][m] times it
+                    const int j = lane >> 2, qd = lane & 3;
+                    float t[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t[e] = (4 * qd + e == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < kCC - 1; ++m) {
+                        const f32x4 col = *reinterpret_cast<const f32x4 *>(at + m * G::LA + 4 * qd);
+                        float x;
+                        switch (m >> 2) {
+                            case 0: x = quad_from<0>(t[m & 3]); break;
+                            case 1: x = quad_from<1>(t[m & 3]); break;
+                            case 2: x = quad_from<2>(t[m & 3]); break;
+                            default: x = quad_from<3>(t[m & 3]); break;
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) t[e] -= col[e] * x;
+                    }
+                    // T^T row j, columns 4 qd .. 4 qd + 3
+                    *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(S + G::oTt) + j * LT +
+                                                4 * qd) =
+                        bf16x4{static_cast<bf16>(t[0]), static_cast<bf16>(t[1]),
+                               static_cast<bf16>(t[2]), static_cast<bf16>(t[3])};
+                } else if (wave == 1) {
+                    // M = Tril(Q+ K-^T): lane (column r, rows i = 4 g4 + e), which is
+                    // M^T as the A operand (row r, k = i); then M^T dO per 16 columns
+                    f32x4 m = zero4();
+#pragma unroll
+                    for (int b = 0; b < D / 32; ++b) m = mma32(row8(qpr, b, g4), row8(kmr, b, g4), m);
+                    f32x4 mv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mv[e] = r <= 4 * g4 + e ? m[e] : 0.f;
+                    const i16x4 mt = pk4(mv);
+                    const bf16 *dot = reinterpret_cast<const bf16 *>(S + G::oDOT);
+#pragma unroll
+                    for (int u = 0; u < G::SW; ++u) {
+                        const f32x4 d = mma16(mt, row4(dot + (16 * u + r) * LT, g4), zero4());
+                        *reinterpret_cast<f32x4 *>(S + G::oDM + (u * 64 + lane) * 16) = d;
+                    }
+                }
+            }
+            __syncthreads();  // B
+        }
+    } else {
+        // ======================================================== scan
+        const int sw = wave - G::PW;
+        const int vl = 16 * sw + r;             // value column within this half
+        const int vg = half * G::DV + vl;       // value column of the head
+        f32x4 dS[NT];  // dL/dS: key rows 16 t + 4 g4 + e, value column vg
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            dS[t] = d_final ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vg * D +
+                                                               16 * t + 4 * g4)
+                            : zero4();
+        for (int tick = 0; tick <= nch && nch > 0; ++tick) {
+            const int c = nch - tick;  // the chunk carried in this tick
+            const unsigned char *S = set_at((tick + 1) & 1);
+            f32x4 u[NT];
+            i16x4 dxp;
+            if (tick > 0) {
+                // the chunk's end gradient for the gradient kernel
+                bf16 *dst = dck + c * ck_stride + (int64_t)vg * D + 4 * g4;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    *reinterpret_cast<bf16x4 *>(dst + 16 * t) =
+                        bf16x4{static_cast<bf16>(dS[t][0]), static_cast<bf16>(dS[t][1]),
+                               static_cast<bf16>(dS[t][2]), static_cast<bf16>(dS[t][3])};
+                // Q+^T dO (no dS in it)
+                const i16x4 dof = row4(reinterpret_cast<const bf16 *>(S + G::oDOT) + vl * LT, g4);
+                const bf16 *qpt = reinterpret_cast<const bf16 *>(S + G::oQpT);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) u[t] = mma16(row4(qpt + (16 * t + r) * LT, g4), dof, zero4());
+                // ddl = M^T dO + Ke dS
+                f32x4 ddl = *reinterpret_cast<const f32x4 *>(S + G::oDM + (sw * 64 + lane) * 16);
+                const bf16 *ke = reinterpret_cast<const bf16 *>(S + G::oKe) + r * LR;
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b) ddl = mma32(row8(ke, b, g4), pk8(dS[2 * b], dS[2 * b + 1]), ddl);
+                // lam = T^T ddl, dX = b lam
+                const f32x4 lam = mma16(row4(reinterpret_cast<const bf16 *>(S + G::oTt) + r * LT, g4),
+                                        pk4(ddl), zero4());
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(
+                    reinterpret_cast<const float *>(S + G::oBeta) + 4 * g4);
+                f32x4 dx;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dx[e] = bt[e] * lam[e];
+                dxp = pk4(dx);
+            }
+            __syncthreads();  // A
+            if (tick > 0) {
+                // dS <- diag(gam) dS + Q+^T dO - K+^T dX
+                const bf16 *kpt = reinterpret_cast<const bf16 *>(S + G::oKpT);
+                const float *gam = reinterpret_cast<const float *>(S + G::oGam);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const f32x4 y = mma16(row4(kpt + (16 * t + r) * LT, g4), dxp, zero4());
+                    const f32x4 gm = *reinterpret_cast<const f32x4 *>(gam + 16 * t + 4 * g4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dS[t][e] = gm[e] * dS[t][e] + u[t][e] - y[e];
+                }
+            }
+            __syncthreads();  // B
+        }
+        if (d_initial) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                *reinterpret_cast<f32x4 *>(d_initial + sbase + (int64_t)vg * D + 16 * t + 4 * g4) =
+                    dS[t];
+        }
+    }
+}
+
+}  // namespace
+
+int launch_bwd_chain(const void *q, const void *k, const float *log_alpha, const float *beta,
+                     const int32_t *cu_seqlens, const void *d_out, const float *d_final_state,
+                     float *d_initial_state, float *dckpt, int32_t num_seqs, int32_t seq_len,
+                     int32_t total_tokens, int32_t num_heads, int head_dim, hipStream_t stream) {
+    const int64_t units64 = (int64_t)num_seqs * num_heads;
+    if (units64 == 0) return 0;
+    if (units64 > (int64_t)1 << 29) return -1;
+    const int units = (int)units64, per_xcd = (units + 7) / 8;
+    const dim3 grid((unsigned)(16 * per_xcd));
+#define KDA_CHAIN_ARGS                                                                         \
+    static_cast<const bf16 *>(q), static_cast<const bf16 *>(k), log_alpha, beta, cu_seqlens,    \
+        static_cast<const bf16 *>(d_out), d_final_state, d_initial_state,                      \
+        reinterpret_cast<bf16 *>(dckpt), num_seqs, seq_len, total_tokens, num_heads, units,    \
+        per_xcd
+    if (head_dim == 128)
+        hipLaunchKernelGGL((bwd_chain_kernel<128>), grid, dim3(ChainCfg<128>::THREADS), 0, stream,
+                           KDA_CHAIN_ARGS);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<64>), grid, dim3(ChainCfg<64>::THREADS), 0, stream,
+                           KDA_CHAIN_ARGS);
+#undef KDA_CHAIN_ARGS
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace kda

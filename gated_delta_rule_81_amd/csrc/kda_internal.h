@@ -104,6 +104,17 @@ int launch_bwd_seq(const void *q, const void *k, const void *v, const float *log
                    int32_t total_tokens, int32_t num_heads, int head_dim, int dtype,
                    hipStream_t stream);
 
+// The chunked backward's dL/dS chain for bf16 inputs (bf16 checkpoints): one
+// workgroup per (sequence, head, half of the value columns), preparation waves
+// one chunk ahead of the scan waves.  Writes the gradient at every 16-token
+// chunk's end to dckpt (the backward workspace's second region, bf16
+// [slot][H][d_v][d_k]) and d_initial_state (if not NULL).  Returns 0, or -1 if
+// the launch failed.
+int launch_bwd_chain(const void *q, const void *k, const float *log_alpha, const float *beta,
+                     const int32_t *cu_seqlens, const void *d_out, const float *d_final_state,
+                     float *d_initial_state, float *dckpt, int32_t num_seqs, int32_t seq_len,
+                     int32_t total_tokens, int32_t num_heads, int head_dim, hipStream_t stream);
+
 // Chunked backward: gradients of the prefill's outputs and final states with
 // respect to q, k, v, log_alpha, beta and the initial states.  Sequences as
 // for launch_chunk_fwd (dense when cu_seqlens == NULL).  d_final_state,

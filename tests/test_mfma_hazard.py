@@ -34,7 +34,7 @@ def test_checker_finds_the_probe_chains(tmp_path):
     assert len(chains) == 2  # the padded chain is not reported
 
 
-@pytest.mark.parametrize("src", ["kda_chunk.hip", "kda_bwd.hip", "kda_decode.hip",
+@pytest.mark.parametrize("src", ["kda_chunk.hip", "kda_bwd.hip", "kda_bwd_chain.hip", "kda_decode.hip",
                                  "kda_seq.hip", "kda_segment.hip"])
 def test_library_has_no_short_mixed_mfma_chains(src, tmp_path):
     chains = find_chains(_asm(os.path.join(CSRC, src), tmp_path))
