@@ -69,6 +69,8 @@ def prefill_flop_per_token_head(d=128, C=64):
 KERNEL_FLOP_PER_TOKEN_HEAD = 6 * 128 * 128 + 24576
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_b256.traffic.json")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_bwd_k3_prefill_32k.traffic.json")
+BWD_SOURCES = ("kda_bwd.hip", "kda_bwd_chain.hip", "kda_chunk.hip", "kda_seq.hip", "kda_device.h")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
 
 
@@ -429,9 +431,13 @@ def bench_backward(torch, args):
     # of algorithmic intensity: HBM-bound in principle
     bf = P["q"].dtype == torch.bfloat16
     mpeak = BF16_DENSE_PEAK_TFLOPS if bf else FP32_MFMA_PEAK_TFLOPS
+    # HBM bytes per call from the committed counter summary (K3 shape only,
+    # while the kernel sources are the ones it was taken on)
+    traffic = (measured_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)
+               if args.bwd_workload == "k3_prefill_32k" else None)
     if bf:
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                 "mfma_tflops_algorithmic": tfl, "mfma_frac": tfl / mpeak}
     else:
         roof = {"bound": "mfma", "achieved": tfl, "peak": mpeak, "unit": "TFLOP/s",
