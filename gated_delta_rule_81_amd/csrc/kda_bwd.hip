@@ -353,11 +353,7 @@ __device__ __forceinline__ const float *ckpt_at(const float *base, int64_t off) 
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 // Sum over the 16 lanes of a row group (lanes with equal l / 16).
-__device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
+__device__ __forceinline__ float row16_sum(float x) { return row16_total(x); }
 
 // One thread's raw inputs of a chunk row piece: four elements as stored.
 template <typename T> struct RawIn;
@@ -858,8 +854,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         const f32x4 dkm = PR::ldst_lds(PR::ldst_lds(zero4(), sDM, LS, sQp + 16 * w, LD, lane), sP,
                                       LS, sKp + 16 * w, LD, lane);
         sched_fence();
-        s1 += __shfl_xor(s1, 16, 64);
-        s1 += __shfl_xor(s1, 32, 64);
+        s1 = rows4_sum(s1);
         const float gamk = sGam[kcol];
         const float gl = sG[(kBC - 1) * LD + kcol];
         // dlog_alpha[t] = d/d log alpha_t of every factor e^{G_a - G_b} (a > b) of
@@ -900,13 +895,13 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         ex[2] = pre[0] + pre[1];
         ex[3] = ex[2] + pre[2];
         const float ptot = ex[3] + pre[3];
-        float above = 0.f, below = 0.f;
+        float above = 0.f, below = 0.f, ts[4], tp[4];
+        rows4_gather(suf[0], ts);
+        rows4_gather(ptot, tp);
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            const float ts = __shfl(suf[0], r + 16 * gg, 64);
-            const float tp = __shfl(ptot, r + 16 * gg, 64);
-            if (gg > g4) above += ts;
-            if (gg < g4) below += tp;
+            if (gg > g4) above += ts[gg];
+            if (gg < g4) below += tp[gg];
         }
         // the pairs: R_t = sum_{i >= t} (Q+_i Zm_i(t) + K+_i Zp_i(t)) with
         // Zm_i(t) = sum_{j < t} dM[i][j] K-_j and Zp_i(t) the same with P; this
@@ -926,8 +921,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
                 const float y = qpv[e] * zm[e] + kpv[e] * zp[e];
                 part += 4 * g4 + e >= t ? y : 0.f;
             }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
+            part = rows4_sum(part);
             if ((t >> 2) == g4) rt[t & 3] = part;
         }
 #pragma unroll

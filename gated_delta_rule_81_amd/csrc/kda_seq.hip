@@ -210,8 +210,7 @@ __global__ __launch_bounds__(64 * (DVS / 16)) void chunk_seq_kernel(
                     p += Sm[t][e] * kk[e];
                 }
             }
-            p += __shfl_xor(p, 16, 64);
-            p += __shfl_xor(p, 32, 64);
+            p = rows4_sum(p);
             const float dl = S[G::oB + j] * (S[G::oV + j * G::LDV + 16 * wave + l16] - p);
             float o = 0.f;
 #pragma unroll
@@ -225,8 +224,7 @@ __global__ __launch_bounds__(64 * (DVS / 16)) void chunk_seq_kernel(
                 }
             }
             if constexpr (MODE == kModeOut) {
-                o += __shfl_xor(o, 16, 64);
-                o += __shfl_xor(o, 32, 64);
+                o = rows4_sum(o);
                 if (l4 == 0) out[((t0 + j) * H + h) * (int64_t)D + vcol] = o;
             }
         }
@@ -448,8 +446,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_seq_kernel(
                 p += S[t][e] * kk[e];
             }
         }
-        p += __shfl_xor(p, 16, 64);
-        p += __shfl_xor(p, 32, 64);
+        p = rows4_sum(p);
         const float dl = sm[G::oB + j] * (sm[G::oV + j * LR + vcol] - p);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -510,8 +507,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_seq_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) p += a[e] * S[t][e] * kk[e];
             }
-            p += __shfl_xor(p, 16, 64);
-            p += __shfl_xor(p, 32, 64);
+            p = rows4_sum(p);
             const float vv = sm[G::oV + j * LR + vcol], dlt = bt * (vv - p);
             const float dov = sm[G::oO + j * LR + vcol];
             // d_delta = G^T k with G = dS + q do^T
@@ -523,8 +519,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_seq_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dd += (dS[t][e] + qq[e] * dov) * kk[e];
             }
-            dd += __shfl_xor(dd, 16, 64);
-            dd += __shfl_xor(dd, 32, 64);
+            dd = rows4_sum(dd);
             // per-key partials of this lane's column, summed over the row's 16
             // columns; lane 15 of each row writes its 4 NT key rows
             float *P = sm + G::oP + (buf * G::W + w) * G::PART;
