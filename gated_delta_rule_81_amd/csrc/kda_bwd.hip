@@ -60,6 +60,7 @@
 
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lanes.h"
 
 namespace kda {
 

@@ -19,6 +19,7 @@
 // (p and o) reduced across the four lane groups.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lanes.h"
 
 namespace kda {
 
