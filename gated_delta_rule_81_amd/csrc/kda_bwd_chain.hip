@@ -30,6 +30,7 @@
 // as the other's accumulator).
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lanes.h"
 
 namespace kda {
 
@@ -199,8 +200,9 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                     acc += rg[j];
                     pre[j] = acc;
                 }
-                const float s0 = __shfl(acc, r, 64), s1 = __shfl(acc, r + 16, 64);
-                const float s2 = __shfl(acc, r + 32, 64), s3 = __shfl(acc, r + 48, 64);
+                float sq[4];  // the four token quarters' sums of this channel
+                rows4_gather(acc, sq);
+                const float s0 = sq[0], s1 = sq[1], s2 = sq[2], s3 = sq[3];
                 const float off = tq == 0 ? 0.f : tq == 1 ? s0 : tq == 2 ? s0 + s1 : (s0 + s1) + s2;
                 const float glast = ((s0 + s1) + s2) + s3;
                 bf16 kp[4], qp[4];
