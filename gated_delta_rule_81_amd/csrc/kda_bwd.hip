@@ -349,6 +349,14 @@ __device__ __forceinline__ const float *ckpt_at(const float *base, int64_t off) 
                : base + off;
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16,
+// fp32 accumulation).  Written as an instruction: the compiler's builtin for it
+// has been seen to take the first pair's registers for every pair of a vector.
+__device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float acc) {
+    asm volatile("v_dot2c_f32_bf16 %0, %1, %2" : "+v"(acc) : "v"(a), "v"(b));
+    return acc;
+}
+
 // Keeps the scheduler from hoisting the LDS reads of later products above
 // this point (which would hold their operands in registers early).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
@@ -825,22 +833,58 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
 #pragma unroll
         for (int hv = 0; hv < NT / 2; ++hv) {
             constexpr int NH = 2;  // tiles per step (a bf16 product's pair)
-            f32x4 Sm[NH], dSm[NH];
+            if constexpr (sizeof(T) == 2) {
+                // bf16 checkpoints: the eight values of a B fragment as loaded
+                // (packed in pairs, no round trip through fp32), the row sum
+                // of S0 * dS_C by two-term bf16 dot products
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const short *cs = reinterpret_cast<const short *>(ckc);
+                const short *ds = reinterpret_cast<const short *>(dckc);
+                s16x8 sv, dv8;
 #pragma unroll
-            for (int t = 0; t < NH; ++t)
+                for (int t = 0; t < NH; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const unsigned off = (unsigned)((16 * (NH * hv + t) + 4 * g4 + e) * D + kcol);
-                    Sm[t][e] = ckpt_load1<T>(ckc, off);
-                    dSm[t][e] = ckpt_load1<T>(dckc, off);
-                }
-            dqs = PR::lds_reg(dqs, sDO + 16 * NH * hv, LD, Sm, lane);
-            xs = PR::lds_reg(xs, sLm + 16 * NH * hv, LD, Sm, lane);
-            dke = PR::lds_reg(dke, sDl + 16 * NH * hv, LD, dSm, lane);
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned off =
+                            (unsigned)((16 * (NH * hv + t) + 4 * g4 + e) * D + kcol);
+                        sv[4 * t + e] = cs[off];
+                        dv8[4 * t + e] = ds[off];
+                    }
+                const bf16x8 sb = __builtin_bit_cast(bf16x8, sv);
+                const bf16x8 db = __builtin_bit_cast(bf16x8, dv8);
+                auto arow = [&](const float *A) {
+                    const float *a0 = A + r * LD + 32 * hv + 4 * g4;
+                    return pack8(*reinterpret_cast<const f32x4 *>(a0),
+                                 *reinterpret_cast<const f32x4 *>(a0 + 16));
+                };
+                dqs = mf32(arow(sDO), sb, dqs);
+                xs = mf32(arow(sLm), sb, xs);
+                dke = mf32(arow(sDl), db, dke);
+                const u32x4 sw = __builtin_bit_cast(u32x4, sv), dw = __builtin_bit_cast(u32x4, dv8);
 #pragma unroll
-            for (int t = 0; t < NH; ++t)
+                for (int pp = 0; pp < 4; ++pp) s1 = dot2_bf16(sw[pp], dw[pp], s1);
+                // (the next step's loads stay below: registers for two
+                // workgroups per CU)
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                f32x4 Sm[NH], dSm[NH];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s1 += Sm[t][e] * dSm[t][e];
+                for (int t = 0; t < NH; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const unsigned off =
+                            (unsigned)((16 * (NH * hv + t) + 4 * g4 + e) * D + kcol);
+                        Sm[t][e] = ckpt_load1<T>(ckc, off);
+                        dSm[t][e] = ckpt_load1<T>(dckc, off);
+                    }
+                dqs = PR::lds_reg(dqs, sDO + 16 * NH * hv, LD, Sm, lane);
+                xs = PR::lds_reg(xs, sLm + 16 * NH * hv, LD, Sm, lane);
+                dke = PR::lds_reg(dke, sDl + 16 * NH * hv, LD, dSm, lane);
+#pragma unroll
+                for (int t = 0; t < NH; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s1 += Sm[t][e] * dSm[t][e];
+            }
             sched_fence();
         }
         // (separate accumulators for the two MFMA shapes, as for ddl above)
@@ -904,26 +948,46 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
             if (gg > g4) above += ts[gg];
             if (gg < g4) below += tp[gg];
         }
-        // the pairs: R_t = sum_{i >= t} (Q+_i Zm_i(t) + K+_i Zp_i(t)) with
-        // Zm_i(t) = sum_{j < t} dM[i][j] K-_j and Zp_i(t) the same with P; this
-        // lane holds rows i = 4 g4 + e, the four lane groups' sums are added
-        float zm[4] = {0.f, 0.f, 0.f, 0.f}, zp[4] = {0.f, 0.f, 0.f, 0.f};
-        float rt[4] = {0.f, 0.f, 0.f, 0.f};
+        // the pairs: R_t = sum_{i >= t} Z_i(t) with Z_i(t) = sum_{j < t} (Q+_i
+        // dM[i][j] + K+_i P[i][j]) K-_j; this lane holds rows i = 4 g4 + e, and
+        // a row leaves the sum (its Z and weights set to zero) at t = i + 1
+        // (qpv and kpv serve as the weights: their last use above is done)
+        float z[4] = {0.f, 0.f, 0.f, 0.f}, *qw = qpv, *kw = kpv;
+        float part[kBC];  // this lane's share of R_t
+        part[0] = 0.f;
 #pragma unroll
         for (int t = 1; t < kBC; ++t) {
             const float km = sKm[(t - 1) * LD + kcol];
             const f32x4 mc = *reinterpret_cast<const f32x4 *>(sDMt + (t - 1) * LS + 4 * g4);
             const f32x4 pc = *reinterpret_cast<const f32x4 *>(sPt + (t - 1) * LS + 4 * g4);
-            float part = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                zm[e] += mc[e] * km;
-                zp[e] += pc[e] * km;
-                const float y = qpv[e] * zm[e] + kpv[e] * zp[e];
-                part += 4 * g4 + e >= t ? y : 0.f;
+            {
+                const int eo = (t - 1) & 3;  // row t - 1 leaves (lane group (t - 1) / 4)
+                const bool out = g4 == ((t - 1) >> 2);
+                z[eo] = out ? 0.f : z[eo];
+                qw[eo] = out ? 0.f : qw[eo];
+                kw[eo] = out ? 0.f : kw[eo];
             }
-            part = rows4_sum(part);
-            if ((t >> 2) == g4) rt[t & 3] = part;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] += (qw[e] * mc[e] + kw[e] * pc[e]) * km;
+            part[t] = (z[0] + z[1]) + (z[2] + z[3]);
+        }
+        // R_t summed over the four lane groups, t = 4 g4 + e left in lane group
+        // g4 (a reduce-scatter by permlane swaps: upper with lower 32 lanes
+        // for t and t + 8, then odd with even rows for t and t + 4)
+        float h8[8], rt[4];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[t]),
+                                                            __float_as_uint(part[t + 8]), false,
+                                                            false);
+            h8[t] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(h8[t]),
+                                                            __float_as_uint(h8[t + 4]), false,
+                                                            false);
+            rt[t] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

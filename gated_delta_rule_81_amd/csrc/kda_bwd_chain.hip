@@ -98,6 +98,14 @@ __device__ __forceinline__ f32x4 mma32(const bf16x8 &a, const bf16x8 &b, f32x4 c
 __device__ __forceinline__ f32x4 mma16(const i16x4 &a, const i16x4 &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// keeps the scheduler from moving LDS accesses across this point
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+// a workgroup barrier that no instruction is scheduled across
+__device__ __forceinline__ void phase_sync() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
 template <int SRC>
 __device__ __forceinline__ float quad_from(float x) {  // lane SRC of each group of 4
     return __int_as_float(
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                                                 4 * dq) = bf16x4{ro[0], ro[1], ro[2], ro[3]};
                 if (tid < kCC) reinterpret_cast<float *>(S + G::oBeta)[tid] = rb;
             }
-            __syncthreads();  // A
+            phase_sync();  // A
             if (c >= 0) {
                 // ---- phase 2: the 16 x 16 work; the next chunk's rows
                 if (c > 0) load(c - 1);
@@ -255,12 +263,19 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                     // comes from quad lane m / 4, and every row below m takes
                     // -A[row][m] times it
                     const int j = lane >> 2, qd = lane & 3;
+                    // all 15 columns in registers first: the substitution's
+                    // steps then wait on no LDS read
+                    f32x4 cols[kCC - 1];
+#pragma unroll
+                    for (int m = 0; m < kCC - 1; ++m)
+                        cols[m] = *reinterpret_cast<const f32x4 *>(at + m * G::LA + 4 * qd);
+                    sched_fence();
                     float t[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) t[e] = (4 * qd + e == j) ? 1.f : 0.f;
 #pragma unroll
                     for (int m = 0; m < kCC - 1; ++m) {
-                        const f32x4 col = *reinterpret_cast<const f32x4 *>(at + m * G::LA + 4 * qd);
+                        const f32x4 col = cols[m];
                         float x;
                         switch (m >> 2) {
                             case 0: x = quad_from<0>(t[m & 3]); break;
@@ -287,14 +302,18 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                     for (int e = 0; e < 4; ++e) mv[e] = r <= 4 * g4 + e ? m[e] : 0.f;
                     const i16x4 mt = pk4(mv);
                     const bf16 *dot = reinterpret_cast<const bf16 *>(S + G::oDOT);
+                    i16x4 dr[G::SW];  // the dO^T rows first, then the products
 #pragma unroll
-                    for (int u = 0; u < G::SW; ++u) {
-                        const f32x4 d = mma16(mt, row4(dot + (16 * u + r) * LT, g4), zero4());
-                        *reinterpret_cast<f32x4 *>(S + G::oDM + (u * 64 + lane) * 16) = d;
-                    }
+                    for (int u = 0; u < G::SW; ++u) dr[u] = row4(dot + (16 * u + r) * LT, g4);
+                    f32x4 d[G::SW];
+#pragma unroll
+                    for (int u = 0; u < G::SW; ++u) d[u] = mma16(mt, dr[u], zero4());
+#pragma unroll
+                    for (int u = 0; u < G::SW; ++u)
+                        *reinterpret_cast<f32x4 *>(S + G::oDM + (u * 64 + lane) * 16) = d[u];
                 }
             }
-            __syncthreads();  // B
+            phase_sync();  // B
         }
     } else {
         // ======================================================== scan
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                 for (int e = 0; e < 4; ++e) dx[e] = bt[e] * lam[e];
                 dxp = pk4(dx);
             }
-            __syncthreads();  // A
+            phase_sync();  // A
             if (tick > 0) {
                 // dS <- diag(gam) dS + Q+^T dO - K+^T dX
                 const bf16 *kpt = reinterpret_cast<const bf16 *>(S + G::oKpT);
@@ -353,7 +372,7 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                     for (int e = 0; e < 4; ++e) dS[t][e] = gm[e] * dS[t][e] + u[t][e] - y[e];
                 }
             }
-            __syncthreads();  // B
+            phase_sync();  // B
         }
         if (d_initial) {
 #pragma unroll
