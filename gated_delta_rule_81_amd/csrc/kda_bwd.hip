@@ -571,7 +571,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
             const float gl = sG[(kBC - 1) * LD + ch];
             const float kr = sKp[tok * LD + ch];
             sKp[tok * LD + ch] = kr * eg;
-            sKm[tok * LD + ch] = kr / eg;
+            sKm[tok * LD + ch] = kr * __expf(-gm);  // (no division)
             sKe[tok * LD + ch] = kr * __expf(gl - gm);
             if (with_grad) sQp[tok * LD + ch] *= eg;
             if (BMODE != kBwdGrad && with_grad) {  // A operands of the dS products
@@ -919,7 +919,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
             kpv[e] = sKp[tok * LD + kcol];
             const float dkp = pkm[e] - xs[e];
             const float qv = dqp[e] * eg;
-            const float kv = dkp * eg + dkm[e] / eg + dke[e] * __expf(gl - gm);
+            const float kv = dkp * eg + dkm[e] * __expf(-gm) + dke[e] * __expf(gl - gm);
             suf[e] = dqs[e] * qpv[e] - xs[e] * kpv[e];
             pre[e] = dke[e] * sKe[tok * LD + kcol];
             if (tok < nval) {
