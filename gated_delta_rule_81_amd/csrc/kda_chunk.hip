@@ -1083,11 +1083,15 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             if constexpr (MODE == kModeStates) {
                 // the chunk's entering state (block 2 m) and, if the sequence has
                 // a block 2 m + 1, the state after block 0:
-                // e^{rho} S + (K e^{rho - Gamma})_{block 0}^T Delta_0
+                // e^{rho} S + (K e^{rho - Gamma})_{block 0}^T Delta_0.
+                // (K e^{rho - Gamma})^T Delta is taken as its block-0 and block-1
+                // halves, the second accumulated onto the first (one product
+                // shape): the first half is also the mid-chunk state's product.
+                // The mid test sits outside the tile loop, so that the tiles'
+                // operand reads can run ahead of their products.
                 const int m2 = 2 * (tick - 1);
                 const int nblk = (int)((tend - tbeg + kBS - 1) / kBS);
                 const bool mid = m2 + 1 < nblk;
-                const typename SM::Frag Dbm = SM::b(Dl[0], zero4());
                 const float *cRho =
                     reinterpret_cast<const float *>(smem + G::oO) + ((tick - 1) & 1) * D;
                 // element offset of this lane's four rows; the states are kept in
@@ -1102,20 +1106,81 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     else
                         *reinterpret_cast<f32x4 *>(snapshots + e0) = x;
                 };
-#pragma unroll
-                for (int t = 0; t < G::NRT; ++t) {
-                    put(off + 16 * t, Sm[t]);
-                    if (mid) {
-                        const f32x4 acc =
-                            SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Dbm);
-                        const f32x4 rh = *reinterpret_cast<const f32x4 *>(cRho + 16 * t + 4 * l4);
-                        f32x4 sm;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sm[e] = rh[e] * Sm[t][e] + acc[e];
-                        put(off + blk + 16 * t, sm);
+                auto halves = [&](int t, f32x4 &h0, f32x4 &hf) {
+                    if constexpr (sizeof(T) == 2) {
+                        // block 0 holds elements 0-3 of each lane's fragment
+                        // (tokens 4 g .. 4 g + 3), block 1 elements 4-7
+                        const bf16x8 af = SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane);
+                        const bf16x4 lo{af[0], af[1], af[2], af[3]}, hi{af[4], af[5], af[6], af[7]};
+                        const bf16x4 d0{static_cast<bf16>(Dl[0][0]), static_cast<bf16>(Dl[0][1]),
+                                        static_cast<bf16>(Dl[0][2]), static_cast<bf16>(Dl[0][3])};
+                        const bf16x4 d1{static_cast<bf16>(Dl[1][0]), static_cast<bf16>(Dl[1][1]),
+                                        static_cast<bf16>(Dl[1][2]), static_cast<bf16>(Dl[1][3])};
+                        h0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                            __builtin_bit_cast(i16x4, lo), __builtin_bit_cast(i16x4, d0), zero4(),
+                            0, 0, 0);
+                        hf = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                            __builtin_bit_cast(i16x4, hi), __builtin_bit_cast(i16x4, d1), h0, 0,
+                            0, 0);
+                    } else {
+                        h0 = SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Db0);
+                        hf = SM::mma(h0, SM::a(cKET + 16 * t * G::LDT, G::LDT, 1, lane), Db1);
                     }
+                };
+                // bf16: tiles t and t + 1 stored together, 16 bytes per lane.  A
+                // lane holds keys 16 t + 4 l4 .. + 3 of each tile; one permlane16
+                // swap per packed word gives the even rows (l4 = 2 j) keys 16 t +
+                // 8 j .. + 7 of tile t and the odd rows keys 16 (t + 1) + 8 j .. + 7
+                // of tile t + 1
+                auto put2 = [&](int64_t e0, int t, const f32x4 &x0, const f32x4 &x1) {
+                    const unsigned a0 = pack2(x0[0], x0[1]), a1 = pack2(x0[2], x0[3]);
+                    const unsigned b0 = pack2(x1[0], x1[1]), b1 = pack2(x1[2], x1[3]);
+                    const auto p0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+                    const auto p1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+                    const int64_t k0 = 16 * (t + (l4 & 1)) + 8 * (l4 >> 1);
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<bf16 *>(snapshots) + e0 - 4 * l4 +
+                                               k0) = u32x4{p0[0], p1[0], p0[1], p1[1]};
+                };
+                auto step = [&](int t, bool with_mid) {
+                    // tiles t and t + 1 (bf16) or tile t (fp32)
+                    constexpr int NP = sizeof(T) == 2 ? 2 : 1;
+                    f32x4 h0[NP], hf[NP], sm[NP];
+#pragma unroll
+                    for (int u = 0; u < NP; ++u) {
+                        halves(t + u, h0[u], hf[u]);
+                        if (with_mid) {
+                            const f32x4 rh =
+                                *reinterpret_cast<const f32x4 *>(cRho + 16 * (t + u) + 4 * l4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sm[u][e] = rh[e] * Sm[t + u][e] + h0[u][e];
+                        }
+                    }
+                    if constexpr (NP == 2) {
+                        put2(off, t, Sm[t], Sm[t + 1]);
+                        if (with_mid) put2(off + blk, t, sm[0], sm[1]);
+                    } else {
+                        put(off + 16 * t, Sm[t]);
+                        if (with_mid) put(off + blk + 16 * t, sm[0]);
+                    }
+#pragma unroll
+                    for (int u = 0; u < NP; ++u) {
+                        const f32x4 gm = *reinterpret_cast<const f32x4 *>(cGam + 16 * (t + u) + 4 * l4);
+                        const f32x4 f1 = *reinterpret_cast<const f32x4 *>(cF1 + 16 * (t + u) + 4 * l4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            Sm[t + u][e] = gm[e] * Sm[t + u][e] + f1[e] * hf[u][e];
+                    }
+                };
+                constexpr int TS = sizeof(T) == 2 ? 2 : 1;  // tiles per step
+                static_assert(G::NRT % TS == 0, "tile pairs");
+                if (mid) {
+#pragma unroll
+                    for (int t = 0; t < G::NRT; t += TS) step(t, true);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < G::NRT; t += TS) step(t, false);
                 }
-            }
+            } else {
 #pragma unroll
             for (int t = 0; t < G::NRT; ++t) {
                 f32x4 acc = SM::mma(zero4(), SM::a(cKET + 16 * t * G::LDT, G::LDT, 0, lane), Db0);
@@ -1125,6 +1190,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 const f32x4 f1 = *reinterpret_cast<const f32x4 *>(cF1 + 16 * t + 4 * l4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sm[t][e] = gm[e] * Sm[t][e] + f1[e] * acc[e];
+            }
             }
             }
             // a snapshot after every snap_every tokens (a multiple of the chunk
