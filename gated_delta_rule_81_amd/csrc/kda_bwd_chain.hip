@@ -45,6 +45,7 @@ struct ChainCfg {
     static constexpr int SW = DV / 16;   // scan waves: 16 value columns each
     static constexpr int THREADS = 64 * (PW + SW);
     static constexpr int NT = D / 16;    // 16-row key tiles of a scan lane's state
+    static_assert(NT % 2 == 0, "key tiles are stored in pairs");
     static constexpr int LR = D + 8;     // bf16 row stride of [16][D] arrays
     static constexpr int LT = 24;        // bf16 row stride of [x][16 tokens] arrays
     // one operand set (byte offsets)
@@ -76,6 +77,10 @@ __device__ __forceinline__ bf16x8 row8(const bf16 *row, int b, int g) {
 // 4 bf16 of a row: k = 4 g + e (the 16x16x16 operand of lane group g)
 __device__ __forceinline__ i16x4 row4(const bf16 *row, int g) {
     return __builtin_bit_cast(i16x4, *reinterpret_cast<const u32x2 *>(row + 4 * g));
+}
+// two floats as bf16 in one word (the first in the low half)
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    return __builtin_bit_cast(unsigned, bf16x2{static_cast<bf16>(a), static_cast<bf16>(b)});
 }
 __device__ __forceinline__ i16x4 pk4(const f32x4 &x) {
     bf16x4 r;
@@ -332,13 +337,21 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
             f32x4 u[NT];
             i16x4 dxp;
             if (tick > 0) {
-                // the chunk's end gradient for the gradient kernel
-                bf16 *dst = dck + c * ck_stride + (int64_t)vg * D + 4 * g4;
+                // the chunk's end gradient for the gradient kernel, key tiles t and
+                // t + 1 together, 16 bytes per lane: one permlane16 swap per packed
+                // word gives the even rows (g4 = 2 j) keys 16 t + 8 j .. + 7 of tile
+                // t and the odd rows keys 16 (t + 1) + 8 j .. + 7 of tile t + 1
+                bf16 *dst = dck + c * ck_stride + (int64_t)vg * D;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    *reinterpret_cast<bf16x4 *>(dst + 16 * t) =
-                        bf16x4{static_cast<bf16>(dS[t][0]), static_cast<bf16>(dS[t][1]),
-                               static_cast<bf16>(dS[t][2]), static_cast<bf16>(dS[t][3])};
+                for (int t = 0; t < NT; t += 2) {
+                    const unsigned a0 = pack2(dS[t][0], dS[t][1]), a1 = pack2(dS[t][2], dS[t][3]);
+                    const unsigned b0 = pack2(dS[t + 1][0], dS[t + 1][1]);
+                    const unsigned b1 = pack2(dS[t + 1][2], dS[t + 1][3]);
+                    const auto p0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+                    const auto p1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+                    *reinterpret_cast<u32x4 *>(dst + 16 * (t + (g4 & 1)) + 8 * (g4 >> 1)) =
+                        u32x4{p0[0], p1[0], p0[1], p1[1]};
+                }
                 // Q+^T dO (no dS in it)
                 const i16x4 dof = row4(reinterpret_cast<const bf16 *>(S + G::oDOT) + vl * LT, g4);
                 const bf16 *qpt = reinterpret_cast<const bf16 *>(S + G::oQpT);
