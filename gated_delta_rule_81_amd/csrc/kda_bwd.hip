@@ -201,6 +201,25 @@ __device__ __forceinline__ f32x4 mf16(const i16x4 &a, const i16x4 &b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// fp32 A rows from LDS (packed to bf16 here) times B tiles of four bf16 as
+// loaded (tile t: k = 16 t + 4 g + e), contraction 16 NT
+template <int NT>
+__device__ __forceinline__ f32x4 mm_lds_raw(f32x4 acc, const float *A, int lda,
+                                            const u32x2 (&B)[NT], int lane) {
+    static_assert(NT % 2 == 0, "bf16 products take tiles in pairs");
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < NT / 2; ++b) {
+        const float *a0 = A + r * lda + 32 * b + 4 * g;
+        acc = mf32(pack8(*reinterpret_cast<const f32x4 *>(a0),
+                         *reinterpret_cast<const f32x4 *>(a0 + 16)),
+                   __builtin_bit_cast(bf16x8, u32x4{B[2 * b][0], B[2 * b][1], B[2 * b + 1][0],
+                                                    B[2 * b + 1][1]}),
+                   acc);
+    }
+    return acc;
+}
+
 template <bool BF>
 struct Prod;
 
@@ -727,15 +746,41 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         // the S orientation, loaded after the staging (whose triangular solve
         // needs the registers; the CU's other workgroup covers the latency)
         const float *ckc = ckpt_at<T>(ck, s0), *dckc = ckpt_at<T>(dck, s0);
+        // bf16 checkpoints: key tiles t and t + 1 as one 16-byte load per lane
+        // (the even lane rows, g4 = 2 i, read keys 16 t + 8 i .. + 7 of tile t,
+        // the odd rows keys 16 (t + 1) + 8 i .. + 7 of tile t + 1), one
+        // permlane16 swap per word pair giving each lane its four keys of both
+        // tiles, kept as loaded (the B operands of their products)
+        constexpr bool RAW = GRAD && sizeof(T) == 2;
+        u32x2 Sr[NT], dSr[NT];
+        if constexpr (RAW) {
+            const bf16 *cb = reinterpret_cast<const bf16 *>(ckc);
+            const bf16 *db = reinterpret_cast<const bf16 *>(dckc);
+            auto pair = [&](const bf16 *base, int t, u32x2 (&out)[NT]) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                    base + (unsigned)(vcol * D + 16 * (t + (g4 & 1)) + 8 * (g4 >> 1)));
+                const auto p0 = __builtin_amdgcn_permlane16_swap(w[0], w[2], false, false);
+                const auto p1 = __builtin_amdgcn_permlane16_swap(w[1], w[3], false, false);
+                out[t] = u32x2{p0[0], p1[0]};
+                out[t + 1] = u32x2{p0[1], p1[1]};
+            };
 #pragma unroll
-        for (int t = 0; t < NT && GRAD; ++t) {
+            for (int t = 0; t < NT; t += 2) {
+                pair(cb, t, Sr);
+                pair(db, t, dSr);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT && GRAD && !RAW; ++t) {
             Ss[t] = ckpt_load4<T>(ckc, (unsigned)(vcol * D + 16 * t + 4 * g4));
             dSs[t] = ckpt_load4<T>(dckc, (unsigned)(vcol * D + 16 * t + 4 * g4));
         }
         // value-column products (this wave's 16 columns of X, Delta, lam, dX)
         f32x4 x = zero4(), dl = zero4();
         if constexpr (GRAD) {
-            const f32x4 pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
+            f32x4 pk;
+            if constexpr (RAW) pk = mm_lds_raw(zero4(), sKp, LD, Sr, lane);
+            else pk = PR::lds_reg(zero4(), sKp, LD, Ss, lane);
             f32x4 xb;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -752,7 +797,8 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         // input on gfx950 (half the accumulator rows then read stale values;
         // tests/hip/mfma_chain.hip); the library never chains the shapes
         const f32x4 ddm = PR::ldst_lds(zero4(), sM, LS, sDO + (vcol - r), LD, lane);
-        if constexpr (PARTS == 1) dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
+        if constexpr (RAW) dde = mm_lds_raw(zero4(), sKe, LD, dSr, lane);
+        else if constexpr (PARTS == 1) dde = PR::lds_reg(zero4(), sKe, LD, dSs, lane);
         f32x4 ddl;
         if constexpr (PARTS > 1) {
             // the partials of the waves with the same value columns (one per
