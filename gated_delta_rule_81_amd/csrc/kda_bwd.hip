@@ -553,9 +553,10 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         R.b = tid < kBC && tid < nval ? (beta + t0 * H + h)[(unsigned)tid * H] : 0.f;
         return R;
     };
-    // `late` runs in every wave after its share of the 16 x 16 work, before the
-    // closing barrier (the waves without such work run it while wave 0 solves)
-    auto prep = [&](int c, bool with_grad, const RawIn<T> &R, auto &&late) -> int {
+    // `early` runs in every wave once the scaled rows are staged, before the
+    // 16 x 16 work; `late` after its share of that work, before the closing
+    // barrier (the waves without such work run both while wave 0 solves)
+    auto prep = [&](int c, bool with_grad, const RawIn<T> &R, auto &&early, auto &&late) -> int {
         const int64_t t0 = tbeg + (int64_t)c * kBC;
         const int nval = (int)((tend - t0) < kBC ? (tend - t0) : kBC);
         {
@@ -599,6 +600,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
             }
         }
         __syncthreads();
+        early();
         if (w == 0) {
             const f32x4 b = PR::template lds_ldst<D>(zero4(), sKp, LD, sKm, LD, lane);
 #pragma unroll
@@ -669,7 +671,7 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
                                     initial_state + sbase + (int64_t)vcol * D + 16 * t + 4 * g4)
                               : zero4();
     for (int c = 0; BMODE == kBwdChain && !states_ready && c < nch; ++c) {
-        prep(c, false, raw_load(c, false, true), [] {});
+        prep(c, false, raw_load(c, false, true), [] {}, [] {});
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             ckpt_store<T>(ck, c * ck_stride + (int64_t)vcol * D + 16 * t + 4 * g4, Ss[t]);
@@ -731,43 +733,55 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
                               dSs[t]);
         }
         const int64_t s0 = c * ck_stride;  // element offset of S0 in the checkpoints
+        // the gradient kernel: the chunk's entering state and end gradient in
+        // the S orientation
+        const float *ckc = ckpt_at<T>(ck, s0), *dckc = ckpt_at<T>(dck, s0);
+        // bf16 checkpoints: key tiles t and t + 1 as one 16-byte load per lane
+        // (the even lane rows, g4 = 2 i, read keys 16 t + 8 i .. + 7 of tile t,
+        // the odd rows keys 16 (t + 1) + 8 i .. + 7 of tile t + 1), issued
+        // before the staging's 16 x 16 work so that their latency runs beside
+        // wave 0's triangular solve; then one permlane16 swap per word pair
+        // gives each lane its four keys of both tiles, kept as loaded (the B
+        // operands of their products)
+        constexpr bool RAW = GRAD && sizeof(T) == 2;
+        u32x4 cw[NT / 2], dcw[NT / 2];
+        auto issue = [&] {
+            if constexpr (RAW) {
+                const bf16 *cb = reinterpret_cast<const bf16 *>(ckc);
+                const bf16 *db = reinterpret_cast<const bf16 *>(dckc);
+#pragma unroll
+                for (int p = 0; p < NT / 2; ++p) {
+                    const unsigned off =
+                        (unsigned)(vcol * D + 16 * (2 * p + (g4 & 1)) + 8 * (g4 >> 1));
+                    cw[p] = *reinterpret_cast<const u32x4 *>(cb + off);
+                    dcw[p] = *reinterpret_cast<const u32x4 *>(db + off);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
         // the split chain's K_end dS partial (K_end is staged before the 16 x 16
         // work), published for the partner waves before prep's closing barrier
         f32x4 *sx = reinterpret_cast<f32x4 *>(sm + G::oXC);
         f32x4 dde = zero4();
-        const int nval = prep(c, true, cur, [&] {
+        const int nval = prep(c, true, cur, issue, [&] {
             if constexpr (PARTS > 1) {
                 dde = PR::lds_reg(zero4(), sKe + 16 * NTW * kh, LD, dSs, lane);
                 sx[w * 64 + lane] = dde;
             }
         });
         const int64_t t0 = tbeg + (int64_t)c * kBC;
-        // the gradient kernel: the chunk's entering state and end gradient in
-        // the S orientation, loaded after the staging (whose triangular solve
-        // needs the registers; the CU's other workgroup covers the latency)
-        const float *ckc = ckpt_at<T>(ck, s0), *dckc = ckpt_at<T>(dck, s0);
-        // bf16 checkpoints: key tiles t and t + 1 as one 16-byte load per lane
-        // (the even lane rows, g4 = 2 i, read keys 16 t + 8 i .. + 7 of tile t,
-        // the odd rows keys 16 (t + 1) + 8 i .. + 7 of tile t + 1), one
-        // permlane16 swap per word pair giving each lane its four keys of both
-        // tiles, kept as loaded (the B operands of their products)
-        constexpr bool RAW = GRAD && sizeof(T) == 2;
         u32x2 Sr[NT], dSr[NT];
         if constexpr (RAW) {
-            const bf16 *cb = reinterpret_cast<const bf16 *>(ckc);
-            const bf16 *db = reinterpret_cast<const bf16 *>(dckc);
-            auto pair = [&](const bf16 *base, int t, u32x2 (&out)[NT]) {
-                const u32x4 w = *reinterpret_cast<const u32x4 *>(
-                    base + (unsigned)(vcol * D + 16 * (t + (g4 & 1)) + 8 * (g4 >> 1)));
-                const auto p0 = __builtin_amdgcn_permlane16_swap(w[0], w[2], false, false);
-                const auto p1 = __builtin_amdgcn_permlane16_swap(w[1], w[3], false, false);
+            auto split = [&](const u32x4 &x, int t, u32x2 (&out)[NT]) {
+                const auto p0 = __builtin_amdgcn_permlane16_swap(x[0], x[2], false, false);
+                const auto p1 = __builtin_amdgcn_permlane16_swap(x[1], x[3], false, false);
                 out[t] = u32x2{p0[0], p1[0]};
                 out[t + 1] = u32x2{p0[1], p1[1]};
             };
 #pragma unroll
-            for (int t = 0; t < NT; t += 2) {
-                pair(cb, t, Sr);
-                pair(db, t, dSr);
+            for (int p = 0; p < NT / 2; ++p) {
+                split(cw[p], 2 * p, Sr);
+                split(dcw[p], 2 * p, dSr);
             }
         }
 #pragma unroll
