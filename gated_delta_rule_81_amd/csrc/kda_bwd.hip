@@ -390,7 +390,9 @@ template <> struct RawIn<bf16> {
     W q, k, v, o;
     f32x4 g;
     float b;
-    __device__ static W ld(const bf16 *p) { return *reinterpret_cast<const W *>(p); }
+    __device__ static W ld(const bf16 *p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const W *>(p));
+    }
     __device__ static W zero() { return W{0u, 0u}; }
     __device__ static f32x4 f32(const W &w) {
         return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
@@ -402,7 +404,9 @@ template <> struct RawIn<float> {
     W q, k, v, o;
     f32x4 g;
     float b;
-    __device__ static W ld(const float *p) { return *reinterpret_cast<const W *>(p); }
+    __device__ static W ld(const float *p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const W *>(p));
+    }
     __device__ static W zero() { return zero4(); }
     __device__ static f32x4 f32(const W &w) { return w; }
 };
@@ -548,9 +552,12 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
         R.q = with_grad && ok ? RawIn<T>::ld(q + rb + li) : RawIn<T>::zero();
         R.k = ok ? RawIn<T>::ld(k + rb + li) : RawIn<T>::zero();
         R.v = with_v && ok ? RawIn<T>::ld(v + rb + li) : RawIn<T>::zero();
-        R.g = ok ? *reinterpret_cast<const f32x4 *>(log_alpha + rb + li) : zero4();
+        R.g = ok ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(log_alpha + rb + li))
+                 : zero4();
         R.o = with_grad && ok ? RawIn<T>::ld(d_out + rb + li) : RawIn<T>::zero();
-        R.b = tid < kBC && tid < nval ? (beta + t0 * H + h)[(unsigned)tid * H] : 0.f;
+        R.b = tid < kBC && tid < nval
+                  ? __builtin_nontemporal_load((beta + t0 * H + h) + (unsigned)tid * H)
+                  : 0.f;
         return R;
     };
     // `early` runs in every wave once the scaled rows are staged, before the
@@ -907,8 +914,8 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
                     for (int e = 0; e < 4; ++e) {
                         const unsigned off =
                             (unsigned)((16 * (NH * hv + t) + 4 * g4 + e) * D + kcol);
-                        sv[4 * t + e] = cs[off];
-                        dv8[4 * t + e] = ds[off];
+                        sv[4 * t + e] = __builtin_nontemporal_load(cs + off);
+                        dv8[4 * t + e] = __builtin_nontemporal_load(ds + off);
                     }
                 const bf16x8 sb = __builtin_bit_cast(bf16x8, sv);
                 const bf16x8 db = __builtin_bit_cast(bf16x8, dv8);
