@@ -71,7 +71,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_fwd_k3_prefill_32k.traf
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_decode_step_b256.traffic.json")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kda_chunk_bwd_k3_prefill_32k.traffic.json")
 BWD_SOURCES = ("kda_bwd.hip", "kda_bwd_chain.hip", "kda_chunk.hip", "kda_seq.hip", "kda_device.h",
-               "kda_lanes.h")
+               "kda_lanes.h", "kda_slots.h")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h")
 
 

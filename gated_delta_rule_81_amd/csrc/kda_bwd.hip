@@ -61,12 +61,14 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_lanes.h"
+#include "kda_slots.h"
 
 namespace kda {
 
 namespace {
 
 constexpr int kBC = 16;  // tokens per chunk of the backward
+static_assert(kBC == kSlotTokens, "one workspace slot per chunk");
 
 template <int D, bool GRAD>
 struct BwdCfg {
@@ -461,25 +463,10 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
     const int h = blockIdx.x % H;
     const int kh = w / VG;  // the split chain: this wave's part of the key tiles
     const int vpart = (int)((blockIdx.x / H) % PARTS);  // and its workgroup's value part
-    // first token of sequence m (offsets clamped into [0, total_tokens])
-    auto seq_begin = [&](int m) -> int64_t {
-        if (!cu_seqlens) return (int64_t)m * seq_len;
-        const int a = cu_seqlens[m];
-        return a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
-    };
     int n, cfix = 0;
     if constexpr (BMODE == kBwdGrad) {
-        // the slot's sequence: the last m whose first slot, begin(m) / 16 + m,
-        // is at or before it (bisection; ends for any offsets)
-        const int64_t slot = blockIdx.x / H;
-        int lo = 0, hi = num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (seq_begin(mid) / kBC + mid <= slot) lo = mid;
-            else hi = mid - 1;
-        }
-        n = lo;
-        cfix = (int)(slot - (seq_begin(n) / kBC + n));
+        // the slot's sequence and chunk
+        n = slot_sequence(cu_seqlens, num_seqs, seq_len, total_tokens, blockIdx.x / H, &cfix);
     } else {
         n = (int)(blockIdx.x / H / PARTS);
         if (cu_seqlens && num_seqs <= 64) {
@@ -520,12 +507,12 @@ __global__ __launch_bounds__(64 * (D / 16), (bwd_min_waves_per_simd<D, BMODE>())
     // this sequence's first checkpoint slot, counted in elements of T
     float *ck = sizeof(T) == 2
                     ? reinterpret_cast<float *>(reinterpret_cast<bf16 *>(ckpt) +
-                                                ((tbeg / kBC + n) * H + h) * DD)
-                    : ckpt + ((tbeg / kBC + n) * H + h) * DD;
+                                                (first_slot(tbeg, n) * H + h) * DD)
+                    : ckpt + (first_slot(tbeg, n) * H + h) * DD;
     float *dck = sizeof(T) == 2  // same slots, end gradients
                      ? reinterpret_cast<float *>(reinterpret_cast<bf16 *>(dckpt) +
-                                                 ((tbeg / kBC + n) * H + h) * DD)
-                     : dckpt + ((tbeg / kBC + n) * H + h) * DD;
+                                                 (first_slot(tbeg, n) * H + h) * DD)
+                     : dckpt + (first_slot(tbeg, n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     const unsigned HD = (unsigned)H * D;  // elements between two tokens' rows
     const int64_t sbase = ((int64_t)n * H + h) * DD;
@@ -1108,7 +1095,7 @@ int launch_bwd(const void *q, const void *k, const void *v, const float *log_alp
                int seq_len, int total_tokens, int H, hipStream_t stream) {
     const int64_t units = (int64_t)num_seqs * H;
     if (units == 0) return 0;
-    const int64_t slots = (int64_t)total_tokens / kBC + num_seqs + 1;
+    const int64_t slots = region_slots(total_tokens, num_seqs);
     if (units > (int64_t)1 << 30 || slots * H > (int64_t)1 << 30) return -1;
     // Units whose gates leave the chunked kernels' range are marked (flag words
     // after the two regions) and redone token by token at the end.
@@ -1171,7 +1158,7 @@ int64_t chunk_bwd_workspace_floats(int64_t total_tokens, int64_t num_seqs, int64
                                    int head_dim) {
     // two regions of one state per slot and head (entering states, end
     // gradients), then the out-of-range flag words of every (sequence, head)
-    return 2 * (total_tokens / kBC + num_seqs + 1) * num_heads * head_dim * head_dim +
+    return 2 * region_slots(total_tokens, num_seqs) * num_heads * head_dim * head_dim +
            bwd_far_flag_words(num_seqs, num_heads);
 }
 

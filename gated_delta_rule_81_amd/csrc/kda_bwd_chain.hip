@@ -31,12 +31,14 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_lanes.h"
+#include "kda_slots.h"
 
 namespace kda {
 
 namespace {
 
 constexpr int kCC = 16;  // tokens per chunk
+static_assert(kCC == kSlotTokens, "one workspace slot per chunk");
 
 template <int D>
 struct ChainCfg {
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
     const unsigned HD = (unsigned)H * D;
     const int64_t sbase = ((int64_t)n * H + h) * DD;
     // chunk c's end gradient goes to slot tbeg / 16 + n + c ([slot][H][d_v][d_k])
-    bf16 *dck = dckpt + ((tbeg / kCC + n) * H + h) * DD;
+    bf16 *dck = dckpt + (first_slot(tbeg, n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     auto set_at = [&](int s) { return sm + s * G::SET; };
 

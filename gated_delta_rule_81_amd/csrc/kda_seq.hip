@@ -20,6 +20,7 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_lanes.h"
+#include "kda_slots.h"
 
 namespace kda {
 
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_seq_kernel(
     const int vcol = 16 * w + l16;
     const int64_t DD = (int64_t)D * D, sbase = ((int64_t)n * H + h) * DD;
     // this unit's checkpoint slot j: the state entering 16-token block j, fp32
-    auto slot = [&](int j) { return ckpt + ((tbeg / 16 + n + j) * H + h) * DD; };
+    auto slot = [&](int j) { return ckpt + ((first_slot(tbeg, n) + j) * H + h) * DD; };
 
     // stage block b's rows as fp32 (alpha = e^{log_alpha}); rows past the end
     // are never stepped
