@@ -316,7 +316,8 @@ struct ChunkOffsets {
     }
 };
 
-template <typename T, int D, int DVS, bool SG>
+// WQ: with the q rows (the states-only mode reads none).
+template <bool WQ, typename T, int D, int DVS, bool SG>
 __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS, SG> &R, const ChunkSrc &s,
                                            const ChunkOffsets<T, D, DVS, SG> &o, int wave,
                                            int lane) {
@@ -324,7 +325,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS, SG> &R, const Ch
 #pragma unroll
     for (int i = 0; i < G::IK; ++i) {
         R.k[i] = buf_load<4>(s.k, o.gk[i]);
-        R.q[i] = buf_load<4>(s.q, o.gk[i]);
+        if constexpr (WQ) R.q[i] = buf_load<4>(s.q, o.gk[i]);
     }
 #pragma unroll
     for (int i = 0; i < G::IG; ++i) R.g[i] = buf_load<4>(s.g, o.gg[i]);
@@ -336,7 +337,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<T, D, DVS, SG> &R, const Ch
 }
 
 // The pieces into the staging area (waits for the loads to land).
-template <typename T, int D, int DVS, bool SG>
+template <bool WQ, typename T, int D, int DVS, bool SG>
 __device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS, SG> &R, unsigned char *smem,
                                             const ChunkOffsets<T, D, DVS, SG> &o, int wave,
                                             int lane) {
@@ -347,7 +348,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<T, D, DVS, SG> &R, u
 #pragma unroll
     for (int i = 0; i < G::IK; ++i) {
         st16(smem + G::oRK + o.sk[i], R.k[i]);
-        st16(smem + G::oRQ + o.sk[i], R.q[i]);
+        if constexpr (WQ) st16(smem + G::oRQ + o.sk[i], R.q[i]);
     }
 #pragma unroll
     for (int i = 0; i < G::IG; ++i) st16(smem + G::oRG + o.sg[i], R.g[i]);
@@ -520,6 +521,8 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
     const int nchunks = (int)((tend - tbeg + kC - 1) / kC);
     // the fast kernel marks far units (states mode: for the backward's flags)
     constexpr bool MARK = !FAR;
+    // the states-only mode forms no outputs: no q rows, Q+ or Mqk tiles
+    constexpr bool WQ = MODE != kModeStates;
     if constexpr (FAR) {
         // the fix-up pass: only units the fast kernel marked (the same
         // element for every thread, so the whole workgroup returns together)
@@ -571,11 +574,11 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
         // about as long as one tick).
         ChunkRegs<T, D, DVS, SG> RA, RB;
         if (nchunks > 0) {
-            load_chunk(RA, src(0), offs, wave, lane);
-            stage_chunk(RA, smem, offs, wave, lane);
+            load_chunk<WQ>(RA, src(0), offs, wave, lane);
+            stage_chunk<WQ>(RA, smem, offs, wave, lane);
         }
         __syncthreads();
-        if (nchunks > 1) load_chunk(RB, src(1), offs, wave, lane);
+        if (nchunks > 1) load_chunk<WQ>(RB, src(1), offs, wave, lane);
 
         // one tick: Rl receives chunk tick + 2, Rs (chunk tick + 1) is staged
         auto prep_tick = [&](int tick, ChunkRegs<T, D, DVS, SG> &Rl,
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
             // ------------------------------------------------------ phase 1
             if (on) {
                 // the loads of chunk tick + 2 go out first (staged next tick)
-                if (tick + 2 < nchunks) load_chunk(Rl, src(tick + 2), offs, wave, lane);
+                if (tick + 2 < nchunks) load_chunk<WQ>(Rl, src(tick + 2), offs, wave, lane);
                 // this chunk's rows r and r + 16 from the staging area
                 Raw<G::RW> rk[2], rq[2];
                 float d0[4], d1[4], erho[4];  // gates of rows r, r + 16 (channels c .. c + 3)
@@ -605,17 +608,23 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     if constexpr (G::RW == 2) {
                         const u32x2 a = *reinterpret_cast<const u32x2 *>(
                             smem + G::oRK + row * G::LSK + c * G::SZ);
-                        const u32x2 b = *reinterpret_cast<const u32x2 *>(
-                            smem + G::oRQ + row * G::LSK + c * G::SZ);
                         rk[j].w[0] = a[0]; rk[j].w[1] = a[1];
-                        rq[j].w[0] = b[0]; rq[j].w[1] = b[1];
+                        if constexpr (WQ) {
+                            const u32x2 b = *reinterpret_cast<const u32x2 *>(
+                                smem + G::oRQ + row * G::LSK + c * G::SZ);
+                            rq[j].w[0] = b[0]; rq[j].w[1] = b[1];
+                        }
                     } else {
                         const u32x4 a = *reinterpret_cast<const u32x4 *>(
                             smem + G::oRK + row * G::LSK + c * G::SZ);
-                        const u32x4 b = *reinterpret_cast<const u32x4 *>(
-                            smem + G::oRQ + row * G::LSK + c * G::SZ);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) { rk[j].w[i] = a[i]; rq[j].w[i] = b[i]; }
+                        for (int i = 0; i < 4; ++i) rk[j].w[i] = a[i];
+                        if constexpr (WQ) {
+                            const u32x4 b = *reinterpret_cast<const u32x4 *>(
+                                smem + G::oRQ + row * G::LSK + c * G::SZ);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) rq[j].w[i] = b[i];
+                        }
                     }
                     if constexpr (!SG) {
                         const f32x4 gg = *reinterpret_cast<const f32x4 *>(
@@ -668,39 +677,39 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                     // block 0: chunk-relative K+, Q+, K- and K e^{rho - Gamma}
                     float kp[4], qp[4], km[4];
                     unpack<T, 4>(rk[0], kf);
-                    unpack<T, 4>(rq[0], qf);
+                    if constexpr (WQ) unpack<T, 4>(rq[0], qf);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float ep = fast_exp2(d0[e]), em = fast_exp2(-d0[e]);
                         kp[e] = kf[e] * ep;
-                        qp[e] = qf[e] * ep;
+                        if constexpr (WQ) qp[e] = qf[e] * ep;
                         km[e] = kf[e] * em;
                         kt0[e] = km[e] * erho[e];
                     }
                     st4(pKP + r * G::LDK + pc, kp);
-                    st4(pQP + r * G::LDK + pc, qp);
+                    if constexpr (WQ) st4(pQP + r * G::LDK + pc, qp);
                     st4(sKM + r * G::LDK + pc, km);
                 }
                 {
                     // block 1: K+, Q+, K- relative to rho, chunk-relative K+, Q+
                     float kd[4], qd[4], kp[4], qp[4];
                     unpack<T, 4>(rk[1], kf);
-                    unpack<T, 4>(rq[1], qf);
+                    if constexpr (WQ) unpack<T, 4>(rq[1], qf);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         ep1[e] = fast_exp2(d1[e]);
                         const float em = fast_exp2(-d1[e]);
                         kd[e] = kf[e] * ep1[e];
-                        qd[e] = qf[e] * ep1[e];
+                        if constexpr (WQ) qd[e] = qf[e] * ep1[e];
                         kp[e] = kd[e] * erho[e];
-                        qp[e] = qd[e] * erho[e];
+                        if constexpr (WQ) qp[e] = qd[e] * erho[e];
                         kt1[e] = kf[e] * em;  // K- of block 1 = K e^{rho - Gamma}
                     }
                     st4(pKP + (kBS + r) * G::LDK + pc, kp);
-                    st4(pQP + (kBS + r) * G::LDK + pc, qp);
+                    if constexpr (WQ) st4(pQP + (kBS + r) * G::LDK + pc, qp);
                     st4(sKM + (kBS + r) * G::LDK + pc, kt1);
                     st4(sKD + r * G::LDK + pc, kd);
-                    st4(sQD + r * G::LDK + pc, qd);
+                    if constexpr (WQ) st4(sQD + r * G::LDK + pc, qd);
                 }
                 if (r == kBS - 1) {
                     // row 15 holds both blocks' total decay: a block that decays
@@ -776,7 +785,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tile = wave + u * G::PW;
-                if (!on || tile >= 6) continue;
+                if (!on || tile >= (WQ ? 6 : 3)) continue;  // (no Mqk without outputs)
                 const bool isA = tile < 3;
                 const int t = isA ? tile : tile - 3;  // 0: (0,0), 1: (1,1), 2: (1,0)
                 const int I = t == 0 ? 0 : 1, J = t == 1 ? 1 : 0;
@@ -848,7 +857,7 @@ __global__ __launch_bounds__(64 * (D / 16 + DVS / 16)) void chunk_fwd_kernel(
                 }
             }
             // the next chunk's rows, loaded during phase 1, into the staging area
-            if (tick + 1 < nchunks) stage_chunk(Rs, smem, offs, wave, lane);
+            if (tick + 1 < nchunks) stage_chunk<WQ>(Rs, smem, offs, wave, lane);
             __syncthreads();
         };
         for (int tick = 0; nchunks > 0 && tick <= nchunks; tick += 2) {
