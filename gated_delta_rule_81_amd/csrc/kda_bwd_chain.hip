@@ -64,8 +64,20 @@ struct ChainCfg {
     static constexpr int oKp = 2 * SET, oKm = oKp + 16 * LR * 2, oQp = oKm + 16 * LR * 2;
     static constexpr int LA = 20;                       // fp32 row stride of A^T
     static constexpr int oAt = oQp + 16 * LR * 2;
-    static constexpr int BYTES = oAt + 16 * LA * 4;
-    static_assert(SET % 16 == 0 && oAt % 16 == 0, "16-byte aligned arrays");
+    // two staging buffers of a chunk's rows as stored (k, q bf16 [16][D]; log_alpha
+    // fp32 [16][D]; this half's d_out bf16 [16][DV]; beta [16]), filled by the scan
+    // waves' direct-to-LDS loads two chunks ahead of their preparation
+    // 16-byte pieces per lane: one instruction moves 1 KiB, stored BLK bytes
+    // apart (the pad puts the rows four tokens apart on other LDS banks)
+    static constexpr int NK = 16 * D * 2 / 1024, NG = 16 * D * 4 / 1024, NO = 16 * DV * 2 / 1024;
+    static constexpr int BLK = 1024 + 32;
+    static constexpr int sK = 0, sQ = sK + NK * BLK, sG = sQ + NK * BLK, sO = sG + NG * BLK,
+                         sB = sO + NO * BLK, STG = sB + 16 * 4;
+    static constexpr int oStg = oAt + 16 * LA * 4;
+    static constexpr int BYTES = oStg + 2 * STG;
+    static constexpr int NSTG = 2 * NK + NG + NO;  // instructions per chunk (beta apart)
+    static_assert(STG % 16 == 0 && NO >= 1, "staging layout");
+    static_assert(SET % 16 == 0 && oAt % 16 == 0 && oStg % 16 == 0, "16-byte aligned arrays");
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -107,10 +119,15 @@ __device__ __forceinline__ f32x4 mma16(const i16x4 &a, const i16x4 &b, f32x4 c) 
 }
 // keeps the scheduler from moving LDS accesses across this point
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
-// a workgroup barrier that no instruction is scheduled across
+// a workgroup barrier that no instruction is scheduled across and that
+// waits for the wave's LDS operations only: the staging waves' direct-to-LDS
+// loads stay in flight across it (their issuer waits for them a tick later,
+// before the barrier that precedes their first read)
 __device__ __forceinline__ void phase_sync() {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 template <int SRC>
@@ -175,6 +192,48 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
     bf16 *dck = dckpt + (first_slot(tbeg, n) * H + h) * DD;
     const int64_t ck_stride = (int64_t)H * DD;
     auto set_at = [&](int s) { return sm + s * G::SET; };
+    auto stage_at = [&](int s) { return sm + G::oStg + s * G::STG; };
+    // Preparation wave 2 + sw's share of chunk c's rows (the waves without 16 x
+    // 16 work), into staging buffer b: piece i of NSTG (k, q, log_alpha, then
+    // this half's d_out, 1 KiB each, 16 bytes per lane in row order) for i = sw,
+    // sw + NSW, ...; the last of them also takes beta.  Rows past the chunk's end
+    // read its first row instead (in bounds; the preparation zeroes them).
+    constexpr int NSW = G::PW - 2;
+    auto stage_rows = [&](int c, int b, int sw) {
+        const int64_t t0 = tbeg + (int64_t)c * kCC;
+        const int nv = (int)((tend - t0) < kCC ? (tend - t0) : kCC);
+        const int64_t row0 = (t0 * H + h) * (int64_t)D;
+        unsigned char *B = stage_at(b);
+#pragma unroll
+        for (int i0 = 0; i0 < G::NSTG; i0 += NSW) {
+            const int i = i0 + sw;
+            if (i >= G::NSTG) break;
+            const void *src;
+            unsigned char *dst;
+            if (i < 2 * G::NK) {  // k, q: D / 8 lanes per row
+                const int j = i % G::NK, lr = j * (1024 / (2 * D)) + lane / (D / 8);
+                const int row = lr < nv ? lr : 0;
+                const bf16 *base = i < G::NK ? k : q;
+                src = base + row0 + (int64_t)row * HD + 8 * (lane % (D / 8));
+                dst = B + (i < G::NK ? G::sK : G::sQ) + j * G::BLK;
+            } else if (i < 2 * G::NK + G::NG) {  // log_alpha: D / 4 lanes per row
+                const int j = i - 2 * G::NK, lr = j * (1024 / (4 * D)) + lane / (D / 4);
+                const int row = lr < nv ? lr : 0;
+                src = log_alpha + row0 + (int64_t)row * HD + 4 * (lane % (D / 4));
+                dst = B + G::sG + j * G::BLK;
+            } else {  // this half's d_out: DV / 8 lanes per row
+                const int j = i - 2 * G::NK - G::NG, lr = j * (1024 / (2 * G::DV)) + lane / (G::DV / 8);
+                const int row = lr < nv ? lr : 0;
+                src = d_out + row0 + (int64_t)row * HD + half * G::DV + 8 * (lane % (G::DV / 8));
+                dst = B + G::sO + j * G::BLK;
+            }
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+        }
+        if (sw == NSW - 1 && lane < kCC) {
+            const int row = lane < nv ? lane : 0;
+            __builtin_amdgcn_global_load_lds(beta + (t0 + row) * H + h, B + G::sB, 4, 0, 0);
+        }
+    };
 
     if (wave < G::PW) {
         // ======================================================== preparation
@@ -185,30 +244,46 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
         const bool has_o = tid < 4 * G::DV;
         float rg[4], rb = 0.f;
         bf16 rk[4], rq[4], ro[4];
-        auto load = [&](int c) {
+        // chunk c's rows from staging buffer b (rows past its end as zeros)
+        auto rows = [&](int c, int b) {
             const int64_t t0 = tbeg + (int64_t)c * kCC;
             const int nv = (int)((tend - t0) < kCC ? (tend - t0) : kCC);
-            const int64_t row0 = (t0 * H + h) * (int64_t)D;
+            const unsigned char *B = stage_at(b);
+            // byte offset of row i in a tensor of rows of RB bytes (1 KiB blocks)
+            auto at = [](int i, int RB) { return (i / (1024 / RB)) * G::BLK + (i % (1024 / RB)) * RB; };
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 4 * tq + j;
-                const unsigned off = (unsigned)i * HD + ch;
                 const bool ok = i < nv;
-                rg[j] = ok ? log_alpha[row0 + off] : 0.f;
-                rk[j] = ok ? k[row0 + off] : static_cast<bf16>(0.f);
-                rq[j] = ok ? q[row0 + off] : static_cast<bf16>(0.f);
+                rg[j] = ok ? reinterpret_cast<const float *>(B + G::sG + at(i, 4 * D))[ch] : 0.f;
+                rk[j] = ok ? reinterpret_cast<const bf16 *>(B + G::sK + at(i, 2 * D))[ch]
+                           : static_cast<bf16>(0.f);
+                rq[j] = ok ? reinterpret_cast<const bf16 *>(B + G::sQ + at(i, 2 * D))[ch]
+                           : static_cast<bf16>(0.f);
                 const int io = 4 * dq + j;
-                ro[j] = has_o && io < nv ? d_out[row0 + (unsigned)io * HD + half * G::DV + dv]
-                                         : static_cast<bf16>(0.f);
+                ro[j] = has_o && io < nv
+                            ? reinterpret_cast<const bf16 *>(B + G::sO + at(io, 2 * G::DV))[dv]
+                            : static_cast<bf16>(0.f);
             }
-            rb = tid < kCC && tid < nv ? beta[(t0 + tid) * H + h] : 0.f;
+            rb = tid < kCC && tid < nv ? reinterpret_cast<const float *>(B + G::sB)[tid] : 0.f;
         };
-        if (nch > 0) load(nch - 1);
+        // the rows of the first two chunks prepared (ticks 0 and 1)
+        if (wave >= 2) {
+            if (nch > 0) stage_rows(nch - 1, 0, wave - 2);
+            if (nch > 1) stage_rows(nch - 2, 1, wave - 2);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        if (nch > 0) rows(nch - 1, 0);
         for (int tick = 0; tick <= nch && nch > 0; ++tick) {
             const int c = nch - 1 - tick;  // the chunk prepared in this tick
             unsigned char *S = set_at(tick & 1);
             if (c >= 0) {
-                // ---- phase 1: prefix, exponentials, the operand rows
+                // ---- phase 1: prefix, exponentials, the operand rows (in
+                // registers since the previous tick; waves 0 and 1, which have
+                // the 16 x 16 work in phase 2, read theirs here, where the
+                // preparation waits for the scan)
+                if (wave < 2 && tick > 0) rows(c, tick & 1);
                 float pre[4], acc = 0.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -245,10 +320,20 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                                                 4 * dq) = bf16x4{ro[0], ro[1], ro[2], ro[3]};
                 if (tid < kCC) reinterpret_cast<float *>(S + G::oBeta)[tid] = rb;
             }
+            // the staged rows of the next chunk (issued last tick) have landed
+            // before barrier A: every preparation wave reads them after it
+            if (wave >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             phase_sync();  // A
             if (c >= 0) {
-                // ---- phase 2: the 16 x 16 work; the next chunk's rows
-                if (c > 0) load(c - 1);
+                // ---- phase 2: the 16 x 16 work on waves 0 and 1; the other
+                // waves read the next chunk's rows from its staging buffer into
+                // registers and stage the rows of the chunk prepared two ticks
+                // on (c - 2) into the buffer this chunk's rows came from (read
+                // before barrier A)
+                if (wave >= 2) {
+                    if (c > 0) rows(c - 1, (tick + 1) & 1);
+                    if (c >= 2) stage_rows(c - 2, tick & 1, wave - 2);
+                }
                 const bf16 *kpr = reinterpret_cast<const bf16 *>(sm + G::oKp) + r * LR;
                 const bf16 *kmr = reinterpret_cast<const bf16 *>(sm + G::oKm) + r * LR;
                 const bf16 *qpr = reinterpret_cast<const bf16 *>(sm + G::oQp) + r * LR;
@@ -333,6 +418,7 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
             dS[t] = d_final ? *reinterpret_cast<const f32x4 *>(d_final + sbase + (int64_t)vg * D +
                                                                16 * t + 4 * g4)
                             : zero4();
+        __syncthreads();  // the staging of the first two chunks
         for (int tick = 0; tick <= nch && nch > 0; ++tick) {
             const int c = nch - tick;  // the chunk carried in this tick
             const unsigned char *S = set_at((tick + 1) & 1);
