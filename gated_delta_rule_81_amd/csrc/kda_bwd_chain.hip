@@ -425,6 +425,21 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
             f32x4 u[NT];
             i16x4 dxp;
             if (tick > 0) {
+                // ddl = M^T dO + Ke dS (the dependent chain first; the stores and
+                // Q+^T dO below fill its matrix-core latency)
+                f32x4 ddl = *reinterpret_cast<const f32x4 *>(S + G::oDM + (sw * 64 + lane) * 16);
+                const bf16 *ke = reinterpret_cast<const bf16 *>(S + G::oKe) + r * LR;
+#pragma unroll
+                for (int b = 0; b < D / 32; ++b) ddl = mma32(row8(ke, b, g4), pk8(dS[2 * b], dS[2 * b + 1]), ddl);
+                // lam = T^T ddl, dX = b lam
+                const f32x4 lam = mma16(row4(reinterpret_cast<const bf16 *>(S + G::oTt) + r * LT, g4),
+                                        pk4(ddl), zero4());
+                const f32x4 bt = *reinterpret_cast<const f32x4 *>(
+                    reinterpret_cast<const float *>(S + G::oBeta) + 4 * g4);
+                f32x4 dx;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dx[e] = bt[e] * lam[e];
+                dxp = pk4(dx);
                 // the chunk's end gradient for the gradient kernel, key tiles t and
                 // t + 1 together, 16 bytes per lane: one permlane16 swap per packed
                 // word gives the even rows (g4 = 2 j) keys 16 t + 8 j .. + 7 of tile
@@ -445,20 +460,6 @@ __global__ __launch_bounds__(ChainCfg<D>::THREADS) void bwd_chain_kernel(
                 const bf16 *qpt = reinterpret_cast<const bf16 *>(S + G::oQpT);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) u[t] = mma16(row4(qpt + (16 * t + r) * LT, g4), dof, zero4());
-                // ddl = M^T dO + Ke dS
-                f32x4 ddl = *reinterpret_cast<const f32x4 *>(S + G::oDM + (sw * 64 + lane) * 16);
-                const bf16 *ke = reinterpret_cast<const bf16 *>(S + G::oKe) + r * LR;
-#pragma unroll
-                for (int b = 0; b < D / 32; ++b) ddl = mma32(row8(ke, b, g4), pk8(dS[2 * b], dS[2 * b + 1]), ddl);
-                // lam = T^T ddl, dX = b lam
-                const f32x4 lam = mma16(row4(reinterpret_cast<const bf16 *>(S + G::oTt) + r * LT, g4),
-                                        pk4(ddl), zero4());
-                const f32x4 bt = *reinterpret_cast<const f32x4 *>(
-                    reinterpret_cast<const float *>(S + G::oBeta) + 4 * g4);
-                f32x4 dx;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dx[e] = bt[e] * lam[e];
-                dxp = pk4(dx);
             }
             phase_sync();  // A
             if (tick > 0) {
