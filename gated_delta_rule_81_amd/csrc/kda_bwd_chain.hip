@@ -20,8 +20,12 @@
 //   ddl = M^T dO + Ke dS        (dS in registers, Ke from the set)
 //   lam = T^T ddl,  dX = b lam  (register tiles feed the next product)
 //   dS  = diag(gam) dS + Q+^T dO - K+^T dX.
-// Two barriers per chunk.  One workgroup per (sequence, head, half of the
-// value columns); the scan waves hold 16 value columns each, all d_k rows, as
+// Two barriers per chunk, which wait for LDS operations only.  The chunk's
+// input rows reach the preparation through LDS: six preparation waves stage
+// them two chunks ahead with direct-to-LDS loads (no registers, and no load
+// issue on the waves with the triangular solve), waiting for their own loads
+// before the barrier that precedes the rows' first read.  One workgroup per
+// (sequence, head, half of the value columns); the scan waves hold 16 value columns each, all d_k rows, as
 // fp32 registers.  Before a chunk is processed its dS (the gradient at the
 // chunk's end) is written to the checkpoint slot the gradient kernel reads;
 // after the first chunk dS is the initial state's gradient.  bf16 matrix
