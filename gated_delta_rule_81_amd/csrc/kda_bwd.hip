@@ -373,8 +373,12 @@ __device__ __forceinline__ const float *ckpt_at(const float *base, int64_t off) 
 // acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2c_f32_bf16,
 // fp32 accumulation).  Written as an instruction: the compiler's builtin for it
 // has been seen to take the first pair's registers for every pair of a vector.
+// The compiler does not see a dot instruction inside inline assembly, so the
+// block carries its own wait states: another VALU instruction that reads a dot
+// product's result needs three after it (without them the row sums read stale
+// values whenever the scheduler puts their consumer right behind the block).
 __device__ __forceinline__ float dot2_bf16(unsigned a, unsigned b, float acc) {
-    asm volatile("v_dot2c_f32_bf16 %0, %1, %2" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_dot2c_f32_bf16 %0, %1, %2\n\ts_nop 3" : "+v"(acc) : "v"(a), "v"(b));
     return acc;
 }
 

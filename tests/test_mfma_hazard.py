@@ -39,3 +39,36 @@ def test_checker_finds_the_probe_chains(tmp_path):
 def test_library_has_no_short_mixed_mfma_chains(src, tmp_path):
     chains = find_chains(_asm(os.path.join(CSRC, src), tmp_path))
     assert not chains, chains[:5]
+
+
+def _dot_without_wait_states(asm):
+    """Each v_dot2c_f32_bf16 (written as inline assembly, which the compiler's
+    hazard recognizer does not see) not followed directly by an s_nop of at
+    least three wait states."""
+    lines = [ln.split(";")[0].strip() for ln in asm.splitlines()]
+    lines = [ln for ln in lines if ln and not ln.startswith((".", "//"))]
+    bad = []
+    for i, ln in enumerate(lines):
+        if ln.startswith("v_dot2c_f32_bf16"):
+            nxt = lines[i + 1] if i + 1 < len(lines) else ""
+            ok = nxt.startswith("s_nop") and int(nxt.split()[1], 0) >= 2
+            if not ok:
+                bad.append((i, ln, nxt))
+    return bad
+
+
+def test_checker_finds_a_dot_without_wait_states():
+    asm = "v_dot2c_f32_bf16 v1, v2, v3\nv_add_f32_e32 v4, v1, v1\nv_dot2c_f32_bf16 v1, v2, v3\ns_nop 3\n"
+    bad = _dot_without_wait_states(asm)
+    assert len(bad) == 1 and bad[0][2].startswith("v_add")
+
+
+@pytest.mark.parametrize("src", ["kda_bwd.hip"])
+def test_inline_dot_products_carry_their_wait_states(src, tmp_path):
+    """Another VALU instruction reading a dot product's result needs three wait
+    states; the library's inline v_dot2c_f32_bf16 provides them itself (with a
+    scheduler that puts the consumer right behind it, the row sums of the
+    gradient kernel read stale values otherwise)."""
+    asm = _asm(os.path.join(CSRC, src), tmp_path)
+    assert "v_dot2c_f32_bf16" in asm
+    assert not _dot_without_wait_states(asm)
