@@ -21,8 +21,12 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not ava
 
 
 def _asm(src, tmp_path):
+    # the library's own per-source flags (its scheduler choices), so that the
+    # assembly scanned is the assembly that ships
+    from gated_delta_rule_81_amd.build import SOURCE_FLAGS
     out = str(tmp_path / (os.path.basename(src) + ".s"))
-    subprocess.run([HIPCC, *FLAGS, src, "-o", out], check=True, capture_output=True)
+    extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+    subprocess.run([HIPCC, *FLAGS, *extra, src, "-o", out], check=True, capture_output=True)
     return open(out).read()
 
 
