@@ -30,11 +30,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function",
          "-I", INCLUDE, "-I", CSRC]
-# Per-source flags: the pipelined dL/dS chain is faster with the machine
-# scheduler that favours instruction-level parallelism (its two wave groups
-# meet at barriers twice per 16 tokens); every other kernel keeps the default,
-# which measured faster for them.
-SOURCE_FLAGS = {"kda_bwd_chain.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source flags: the pipelined dL/dS chain and the fp32 token recurrences
+# (kda_seq.hip) are faster with the machine scheduler that favours
+# instruction-level parallelism; the other kernels keep the default, which
+# measured faster for them.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS = {"kda_bwd_chain.hip": _ILP, "kda_seq.hip": _ILP}
 
 
 def _compile(src: str, verbose: bool) -> str:
