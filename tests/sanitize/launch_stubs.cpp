@@ -1,7 +1,7 @@
 // launch_stubs.cpp -- stand-ins for the library's kernel launchers, so that
 // the host validation of kda_api.cpp can be built and run without the GPU
 // code.  Reaching one means a call got past every host and device check on a
-// host without a GPU, which the driver does not expect: abort loudly.
+// host without a GPU, which abi_driver.cpp never expects: abort loudly.
 #include <stdio.h>
 #include <stdlib.h>
 
